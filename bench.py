@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused W4A4 + low-rank linear on one MI355X.
+
+One step = one call of the layer on one batch: twq_quantize_act (per-token
+quantization + T = X L1) then twq_dual_linear (residual int4 GEMM + low-rank
+epilogue), weights pre-packed and resident in HBM. Inputs are synthetic (seeded,
+with the shapes and value distributions of the layer configurations), and the
+steps rotate over enough copies of the weights that the caches (4 MB L2 per
+XCD, 256 MB Infinity Cache) cannot hold the working set.
+
+Prints one JSON line. `value` is effective TOPS = (2bmn + 2br(m+n)) / time per
+step. The `roofline` object prices the dominant kernel (twq_dual_linear)
+against HBM bandwidth (few tokens) or the int8 matrix-core peak (many tokens).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 matrix cores, TOP/s
+ROTATE_BYTES = 512 << 20     # working set that defeats L2 + Infinity Cache reuse
+BASELINE_METRIC = "fused W4A4+low-rank linear: \u00b5s/call, effective TOPS, % int8-MFMA/HBM roofline"
+
+
+def layer_ops(b, m, n, r):
+    """Useful operations of one layer call: the int8 GEMM plus the two low-rank products."""
+    return 2 * b * m * n + 2 * b * r * (m + n)
+
+
+def call_bytes(b, m, n, r):
+    """Compulsory HBM bytes of one whole call: X fp16, Q_W, s_W, L1 and L2 fp16, Y fp16."""
+    return 2 * b * m + m * n // 2 + 4 * n + 2 * r * (m + n) + 2 * b * n
+
+
+def dual_linear_bytes(b, m, n, r):
+    """Algorithmic bytes of one twq_dual_linear launch: it reads Q_X, s_X, Q_W, s_W, T and
+    L2, and writes Y, each once."""
+    return b * m // 2 + 4 * b + m * n // 2 + 4 * n + 4 * b * r + 2 * n * r + 2 * b * n
+
+
+def lowrank_storage_ratio(m, n, r):
+    """fp16 low-rank storage r(m+n) * 2 bytes over the 4-bit residual m n / 2 bytes."""
+    return 2 * r * (m + n) / (m * n / 2)
+
+
+def _cpu_baseline(d, budget_s=12.0):
+    """The oracle (plain C, OpenMP) on the host: per-call work with weights pre-quantized."""
+    import numpy as np
+
+    import oracle
+    x, w, l1t, l2t = d["x"], d["w_res"], d["l1t"], d["l2t"]
+    b, m = x.shape
+    n, r = w.shape[0], l1t.shape[0]
+    qw, _, sw = oracle.quantize_weight(w)  # offline packing, not timed
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        qx, _, sx = oracle.quantize_act(x)
+        acc = oracle.residual_acc(qx, qw)
+        y = sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] * acc
+        if r:
+            y += oracle.lowrank_out(oracle.lowrank_t(x, l1t), l2t)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 1000:
+            break
+    sec = el / calls
+    return {"value": layer_ops(b, m, n, r) / sec / 1e12, "unit": "TOPS", "cores": oracle.max_threads(),
+            "kind": "oracle", "ms_per_call": sec * 1e3,
+            "sample": f"{calls} whole calls of the same workload (b={b}, m={m}, n={n}, r={r}) "
+                      f"in {el:.1f} s; weights quantized once outside the timing"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="o_proj_decode")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate over (0: auto)")
+    ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the layer is benchmarked on one "
+                                   "MI355X; run with --gpus 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a4_rank_gemm_amd as twq
+
+    cfg = synth.CONFIGS[args.config]
+    b, m, n, r = cfg.b, cfg.m, cfg.n, cfg.r
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# generating {args.config}: b={b} m={m} n={n} r={r}", file=sys.stderr, flush=True)
+    d = synth.make_layer(cfg)
+
+    per_copy = call_bytes(b, m, n, r)
+    copies = args.copies or max(1, math.ceil(ROTATE_BYTES / per_copy))
+    x0 = torch.from_numpy(d["x"]).to(dev)
+    w0 = torch.from_numpy(d["w_res"]).to(dev)
+    l10 = torch.from_numpy(d["l1t"]).to(dev) if r else None
+    l20 = torch.from_numpy(d["l2t"]).to(dev) if r else None
+    qw0, sw0 = twq.pack_weight(w0)
+    del w0
+    sets = []
+    for c in range(copies):
+        sets.append({
+            "x": x0.clone(), "qw": qw0.clone(), "sw": sw0.clone(),
+            "l1t": l10.clone() if r else None, "l2t": l20.clone() if r else None,
+            "qx": torch.empty((b, m // 2), dtype=torch.uint8, device=dev),
+            "sx": torch.empty((b,), dtype=torch.float32, device=dev),
+            "t": torch.empty((b, r), dtype=torch.float32, device=dev) if r else None,
+            "y": torch.empty((b, n), dtype=torch.float16, device=dev),
+        })
+    L = twq.lib()
+    ws, wsb = twq._workspace(dev, L.twq_quantize_act_workspace_bytes(b, m, r))
+    P = lambda t: None if t is None else twq.ctypes.c_void_p(t.data_ptr())
+
+    def quant(s, stream):
+        twq._check(L.twq_quantize_act(P(s["x"]), b, m, P(s["qx"]), P(s["sx"]), P(s["l1t"]), r, P(s["t"]),
+                                      P(ws), wsb, stream), "twq_quantize_act")
+
+    def dual(s, stream):
+        twq._check(L.twq_dual_linear(P(s["qx"]), P(s["sx"]), P(s["qw"]), P(s["sw"]), P(s["t"]), P(s["l2t"]), r,
+                                     P(s["y"]), b, m, n, stream), "twq_dual_linear")
+
+    stream = torch.cuda.Stream(dev)  # default priority
+
+    def hs():
+        return twq.ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def steps_fn(k, with_quant=True, offset=0):
+        def run():
+            st = hs()
+            for i in range(k):
+                s = sets[(i + offset) % copies]
+                if with_quant:
+                    quant(s, st)
+                dual(s, st)
+        return run
+
+    def timed(fn_or_graph, is_graph):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if is_graph:
+            fn_or_graph.replay()
+        else:
+            fn_or_graph()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1)  # ms
+
+    with torch.cuda.stream(stream):
+        # one eager call first (lazy initialisation, workspace), then the warmup steps
+        steps_fn(1)()
+        torch.cuda.synchronize()
+        if args.eager:
+            steps_fn(args.warmup)()
+            ms = timed(steps_fn(args.steps), False)
+            ms_dual = timed(steps_fn(args.steps, with_quant=False), False)
+        else:
+            gw = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gw, stream=stream):
+                steps_fn(args.warmup)()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                steps_fn(args.steps)()
+            gd = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gd, stream=stream):
+                steps_fn(args.steps, with_quant=False)()
+            gw.replay()
+            torch.cuda.synchronize()
+            ms = timed(g, True)
+            gd.replay()  # untimed pass of the kernel-only graph
+            ms_dual = timed(gd, True)
+        torch.cuda.synchronize()
+
+    ms_step = ms / args.steps
+    us_dual = ms_dual / args.steps * 1e3
+    ops = layer_ops(b, m, n, r)
+    tops = ops / (ms_step * 1e-3) / 1e12
+    decode = b <= 64
+    if decode:
+        ach = dual_linear_bytes(b, m, n, r) / (us_dual * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        ach = 2 * b * m * n / (us_dual * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": None}
+    roof["kernel"] = "twq_dual_linear"
+    roof["kernel_us"] = round(us_dual, 3)
+
+    out = {
+        "metric": BASELINE_METRIC,
+        "value": round(tops, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "us_per_call": round(ms_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes on i8 MFMA (int32 acc) + fp16 low-rank (fp32 acc)",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: b={b} m={m} n={n} r={r}", "b": b, "m": m, "n": n, "r": r,
+                   "weight_copies_rotated": copies, "launch": "eager" if args.eager else "hip_graph",
+                   "call_bytes": call_bytes(b, m, n, r),
+                   "hbm_frac_whole_call": round(call_bytes(b, m, n, r) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                   "int8_mfma_frac_whole_call": round(2 * b * m * n / (ms_step * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = _cpu_baseline(d)
+        out["cpu_baseline"]["host"] = platform.processor() or platform.machine()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,137 @@
+/*
+ * twq.h -- C ABI of libtwq, the fused W4A4 + low-rank linear layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer is the dual-component linear of TwinQuant ("TwinQuant: Learnable
+ * Subspace Decomposition for 4-Bit LLM Quantization"):
+ *
+ *     Y = s_X s_W (Q_X Q_W) + (X L1) L2
+ *
+ * page 1, section 2, eq. (2) (a 4-bit x 4-bit product with its scales) and
+ * eq. (3) (a residual R quantized to 4 bits plus a low-rank pair U, V), with the
+ * symmetric round-to-nearest quantizer of eq. (1): s = max|v| / q_max, q_max = 7,
+ * q = round(v / s). Following page 1, section 4.3, the residual and low-rank
+ * partial products never reach global memory: one epilogue merges them and
+ * stores fp16 once.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers owned by the caller; the library never frees
+ *    or retains them. Entry points that take a workspace document its size.
+ *  - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *    null stream). No entry point synchronizes. Results are ready when the stream
+ *    reaches them.
+ *  - Arguments are validated before any HIP call; a rejected call launches
+ *    nothing. Kernel launch failures return TWQ_ERR_HIP, and
+ *    twq_last_error_string() gives the HIP text (per calling thread).
+ *    Faults inside a kernel surface at the caller's next synchronization.
+ *  - Non-finite inputs are not supported (the result is unspecified).
+ *  - Every pointer must be 16-byte aligned (TWQ_ERR_ALIGN otherwise).
+ *  - Shapes: b (tokens) >= 0, m (input channels) a positive multiple of 128 and
+ *    at most 131072, n (output channels) >= 0 and a multiple of 16, rank r = 0
+ *    or a multiple of 16 up to 256. b == 0 or n == 0 is a valid empty call that
+ *    launches nothing.
+ *
+ * Data formats:
+ *  - X: fp16 [b][m], row-major (one token per row). Y: fp16 [b][n].
+ *  - Packed 4-bit codes: two per byte, K-contiguous rows; byte t of a row holds
+ *    code 2t in its low nibble and code 2t+1 in its high nibble, each a 4-bit
+ *    two's complement value in [-7, 7].
+ *  - Scales are fp32: s_X one per token, s_W one per output channel.
+ *  - Quantization reading of eq. (1): s = fl32(max|v| / 7), q = round-half-even
+ *    (fl32(v / s)) with correctly rounded binary32 divisions; an all-zero
+ *    vector gets s = 0 and codes 0.
+ */
+#ifndef TWQ_H
+#define TWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TWQ_OK = 0,
+    TWQ_ERR_NULL = 1,        /* a required pointer is NULL */
+    TWQ_ERR_SHAPE = 2,       /* a size is out of the supported range */
+    TWQ_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+    TWQ_ERR_UNSUPPORTED = 4, /* a valid but unsupported combination */
+    TWQ_ERR_HIP = 5,         /* the HIP runtime reported an error */
+    TWQ_ERR_WORKSPACE = 6    /* the workspace is missing or too small */
+} twq_status;
+
+/* Human-readable name of a status code (static storage). */
+const char *twq_status_string(int status);
+
+/* Text of the last TWQ_ERR_HIP on the calling thread ("" if none). */
+const char *twq_last_error_string(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int twq_version(void);
+
+/*
+ * Activation quantizer (eq. (1) per token, page 1, section 2), optionally with
+ * the first low-rank product T = X L1 (eq. (3)).
+ *
+ *   x     fp16 [b][m]                  input activations
+ *   qx    u8   [b][m/2]   (out)        packed 4-bit codes Q_X
+ *   sx    f32  [b]        (out)        per-token scales s_X = max_k |x[i][k]| / 7
+ *   l1t   fp16 [r][m]                  L1 transposed (row t = column t of L1); may be
+ *                                      NULL only when r == 0
+ *   t     f32  [b][r]     (out)        T = X L1 from the fp16 X, fp32 accumulation;
+ *                                      may be NULL only when r == 0
+ *   workspace, workspace_bytes         device scratch of at least
+ *                                      twq_quantize_act_workspace_bytes(b, m, r)
+ *                                      bytes for partial sums of T (may be NULL
+ *                                      when that is 0, as it is for r == 0). No
+ *                                      initial contents are needed. Calls that
+ *                                      share a workspace must not overlap in time.
+ */
+size_t twq_quantize_act_workspace_bytes(int64_t b, int64_t m, int64_t r);
+twq_status twq_quantize_act(const void *x, int64_t b, int64_t m, void *qx, float *sx,
+                            const void *l1t, int64_t r, float *t, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * Offline weight packer (eq. (1) per output channel; the residual R of eq. (3)).
+ *
+ *   w_res f32 [n][m]                   residual weight, one row per output channel
+ *                                      (the transpose of the pages' m x n W)
+ *   qw    u8  [n][m/2]    (out)        packed 4-bit codes Q_W
+ *   sw    f32 [n]         (out)        per-channel scales s_W
+ */
+twq_status twq_pack_weight(const float *w_res, int64_t n, int64_t m, void *qw, float *sw,
+                           void *stream);
+
+/*
+ * The fused layer (eqs. (2)-(3), single epilogue of page 1, section 4.3):
+ *
+ *   Y[i][j] = fp16( s_X[i] s_W[j] sum_k Q_X[i][k] Q_W[j][k] + sum_t T[i][t] L2[t][j] )
+ *
+ * The integer sum is exact (int32 on int8 matrix cores); T is rounded to fp16
+ * for the fp16 matrix cores with fp32 accumulation.
+ *
+ *   qx, sx                              from twq_quantize_act
+ *   qw, sw                              from twq_pack_weight
+ *   t     f32  [b][r]                  from twq_quantize_act; NULL iff r == 0
+ *   l2t   fp16 [n][r]                  L2 transposed (row j = column j of L2); NULL iff r == 0
+ *   y     fp16 [b][n]     (out)
+ */
+twq_status twq_dual_linear(const void *qx, const float *sx, const void *qw, const float *sw,
+                           const float *t, const void *l2t, int64_t r, void *y, int64_t b,
+                           int64_t m, int64_t n, void *stream);
+
+/*
+ * Test export: the same main loop as twq_dual_linear, but the epilogue stores
+ * the exact integer accumulator acc[i][j] = sum_k Q_X[i][k] Q_W[j][k] as int32
+ * [b][n] instead of Y. Used to check the integer path bit for bit.
+ */
+twq_status twq_debug_residual_acc(const void *qx, const void *qw, int32_t *acc, int64_t b,
+                                  int64_t m, int64_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWQ_H */

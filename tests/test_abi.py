@@ -1,0 +1,97 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol include/twq.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4a4_rank_gemm_amd as twq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "twq.h")
+
+OK, NULL, SHAPE, ALIGN, WORKSPACE = 0, 1, 2, 3, 6
+A = ctypes.c_void_p(4096)       # an aligned, never-dereferenced address
+MIS = ctypes.c_void_p(4096 + 8)  # misaligned
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(twq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = twq.lib()
+    declared = _declared()
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(declared) == set(twq.EXPORTS)
+
+
+def test_status_strings_and_version():
+    L = twq.lib()
+    assert L.twq_status_string(0) == b"ok"
+    assert L.twq_status_string(2) == b"unsupported shape"
+    assert L.twq_status_string(99) == b"unknown status"
+    assert L.twq_version() >= 100
+
+
+@pytest.mark.parametrize("b,m,r", [(1, 100, 0), (1, 0, 0), (1, 256, 8), (1, 256, 272), (-1, 256, 0),
+                                   (1, 131072 + 128, 0)])
+def test_quantize_act_rejects_shapes(b, m, r):
+    st = twq.lib().twq_quantize_act(A, b, m, A, A, A, r, A, A, 1 << 30, None)
+    assert st == SHAPE
+
+
+def test_quantize_act_rejects_null_and_alignment():
+    L = twq.lib()
+    assert L.twq_quantize_act(None, 4, 256, A, A, None, 0, None, None, 0, None) == NULL
+    assert L.twq_quantize_act(A, 4, 256, A, A, None, 32, A, None, 0, None) == NULL
+    assert L.twq_quantize_act(MIS, 4, 256, A, A, None, 0, None, None, 0, None) == ALIGN
+    assert L.twq_quantize_act(A, 4, 256, A, A, MIS, 32, A, A, 1 << 30, None) == ALIGN
+
+
+def test_quantize_act_workspace():
+    L = twq.lib()
+    need = L.twq_quantize_act_workspace_bytes(2048, 4096, 32)  # many tokens: K-slice partial sums
+    assert need > 0 and need % (2048 * 32 * 4) == 0
+    assert L.twq_quantize_act_workspace_bytes(2048, 4096, 0) == 0
+    assert L.twq_quantize_act_workspace_bytes(16, 4096, 32) % (16 * 32 * 4) == 0  # few tokens: K slices
+    assert L.twq_quantize_act_workspace_bytes(16, 4096, 0) == 0
+    assert L.twq_quantize_act_workspace_bytes(16, 100, 32) == 0  # invalid shape
+    assert L.twq_quantize_act(A, 2048, 4096, A, A, A, 32, A, None, 0, None) == WORKSPACE
+    assert L.twq_quantize_act(A, 2048, 4096, A, A, A, 32, A, A, need - 1, None) == WORKSPACE
+
+
+def test_empty_calls_are_no_ops():
+    L = twq.lib()
+    assert L.twq_quantize_act(None, 0, 256, None, None, None, 0, None, None, 0, None) == OK
+    assert L.twq_pack_weight(None, 0, 256, None, None, None) == OK
+    assert L.twq_dual_linear(None, None, None, None, None, None, 0, None, 0, 256, 64, None) == OK
+    assert L.twq_dual_linear(None, None, None, None, None, None, 0, None, 8, 256, 0, None) == OK
+    assert L.twq_debug_residual_acc(None, None, None, 0, 256, 16, None) == OK
+
+
+@pytest.mark.parametrize("b,m,n,r", [(4, 256, 24, 0), (4, 200, 32, 0), (4, 256, 32, 48 + 8),
+                                     (1 << 25, 256, 32, 0), (4, 256, -16, 0)])
+def test_dual_linear_rejects_shapes(b, m, n, r):
+    assert twq.lib().twq_dual_linear(A, A, A, A, A, A, r, A, b, m, n, None) == SHAPE
+
+
+def test_dual_linear_rejects_null_and_alignment():
+    L = twq.lib()
+    assert L.twq_dual_linear(A, A, A, A, None, None, 32, A, 4, 256, 32, None) == NULL
+    assert L.twq_dual_linear(A, None, A, A, None, None, 0, A, 4, 256, 32, None) == NULL
+    assert L.twq_dual_linear(A, A, A, A, None, None, 0, MIS, 4, 256, 32, None) == ALIGN
+    assert L.twq_pack_weight(A, 32, 256, MIS, A, None) == ALIGN
+    assert L.twq_pack_weight(A, 24, 256, A, A, None) == SHAPE
+    assert L.twq_debug_residual_acc(A, None, A, 4, 256, 32, None) == NULL
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    x = torch.zeros(4, 256, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        twq.quantize_act(x)

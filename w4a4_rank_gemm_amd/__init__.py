@@ -1,0 +1,207 @@
+"""w4a4_rank_gemm_amd -- the fused W4A4 + low-rank linear of TwinQuant on MI355X.
+
+A thin ctypes binding of libtwq (include/twq.h): it checks tensor dtypes and
+devices, allocates outputs with torch on the input's device, and passes raw
+pointers and the current HIP stream. Every step of the layer runs in the HIP
+kernels of libtwq; there is no fallback. If libtwq.so has not been built, or no
+GPU is present, the calls raise.
+
+    Y = s_X s_W (Q_X Q_W) + (X L1) L2
+
+(TwinQuant, page 1, section 2, eqs. (1)-(3); fused as in page 1, section 4.3.)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libtwq.so")
+
+TWQ_OK = 0
+STATUS_NAMES = {0: "TWQ_OK", 1: "TWQ_ERR_NULL", 2: "TWQ_ERR_SHAPE", 3: "TWQ_ERR_ALIGN",
+                4: "TWQ_ERR_UNSUPPORTED", 5: "TWQ_ERR_HIP", 6: "TWQ_ERR_WORKSPACE"}
+
+# every symbol include/twq.h declares
+EXPORTS = ("twq_status_string", "twq_last_error_string", "twq_version",
+           "twq_quantize_act_workspace_bytes", "twq_quantize_act", "twq_pack_weight",
+           "twq_dual_linear", "twq_debug_residual_acc")
+
+
+class TwqError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        msg = f"{where}: {STATUS_NAMES.get(status, status)}"
+        if detail:
+            msg += f" ({detail})"
+        super().__init__(msg)
+
+
+_lib = None
+_lock = threading.Lock()
+_P, _I, _S = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtwq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise ImportError(f"libtwq.so is not built ({LIB_PATH}); run "
+                                      "`python -c 'import __graft_entry__ as g; g.build()'`")
+                L = ctypes.CDLL(LIB_PATH)
+                L.twq_status_string.restype = ctypes.c_char_p
+                L.twq_status_string.argtypes = [ctypes.c_int]
+                L.twq_last_error_string.restype = ctypes.c_char_p
+                L.twq_last_error_string.argtypes = []
+                L.twq_version.restype = ctypes.c_int
+                L.twq_quantize_act_workspace_bytes.restype = _S
+                L.twq_quantize_act_workspace_bytes.argtypes = [_I, _I, _I]
+                L.twq_quantize_act.restype = ctypes.c_int
+                L.twq_quantize_act.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P, _S, _P]
+                L.twq_pack_weight.restype = ctypes.c_int
+                L.twq_pack_weight.argtypes = [_P, _I, _I, _P, _P, _P]
+                L.twq_dual_linear.restype = ctypes.c_int
+                L.twq_dual_linear.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P]
+                L.twq_debug_residual_acc.restype = ctypes.c_int
+                L.twq_debug_residual_acc.argtypes = [_P, _P, _P, _I, _I, _I, _P]
+                _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != TWQ_OK:
+        detail = lib().twq_last_error_string().decode() if status == 5 else ""
+        raise TwqError(status, where, detail)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# One workspace per (device, stream): calls sharing a workspace must not overlap,
+# and calls enqueued on one stream never do. New workspaces start zeroed.
+_workspaces: dict = {}
+
+
+def _workspace(dev: torch.device, nbytes: int):
+    if nbytes == 0:
+        return None, 0
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws, ws.numel()
+
+
+def quantize_act(x: torch.Tensor, l1t: torch.Tensor | None = None):
+    """X fp16 [b][m] -> (Q_X u8 [b][m/2], s_X f32 [b], T f32 [b][r] or None)."""
+    _need(x, "x", torch.float16, 2)
+    b, m = x.shape
+    r = 0
+    if l1t is not None:
+        _need(l1t, "l1t", torch.float16, 2)
+        r = l1t.shape[0]
+        if l1t.shape[1] != m or l1t.device != x.device:
+            raise ValueError("l1t must be [r][m] on x's device")
+    dev = x.device
+    qx = torch.empty((b, m // 2), dtype=torch.uint8, device=dev)
+    sx = torch.empty((b,), dtype=torch.float32, device=dev)
+    t = torch.empty((b, r), dtype=torch.float32, device=dev) if r else None
+    L = lib()
+    ws, wsb = _workspace(dev, L.twq_quantize_act_workspace_bytes(b, m, r))
+    _check(L.twq_quantize_act(_ptr(x), b, m, _ptr(qx), _ptr(sx), _ptr(l1t), r, _ptr(t),
+                              _ptr(ws), wsb, _stream(dev)), "twq_quantize_act")
+    return qx, sx, t
+
+
+def pack_weight(w_res: torch.Tensor):
+    """W_res f32 [n][m] -> (Q_W u8 [n][m/2], s_W f32 [n])."""
+    _need(w_res, "w_res", torch.float32, 2)
+    n, m = w_res.shape
+    dev = w_res.device
+    qw = torch.empty((n, m // 2), dtype=torch.uint8, device=dev)
+    sw = torch.empty((n,), dtype=torch.float32, device=dev)
+    _check(lib().twq_pack_weight(_ptr(w_res), n, m, _ptr(qw), _ptr(sw), _stream(dev)),
+           "twq_pack_weight")
+    return qw, sw
+
+
+def dual_linear(qx, sx, qw, sw, t=None, l2t=None, out: torch.Tensor | None = None):
+    """The fused layer: Y fp16 [b][n] from the packed operands and the low-rank pair."""
+    _need(qx, "qx", torch.uint8, 2)
+    _need(qw, "qw", torch.uint8, 2)
+    _need(sx, "sx", torch.float32, 1)
+    _need(sw, "sw", torch.float32, 1)
+    b, kb = qx.shape
+    n = qw.shape[0]
+    m = 2 * kb
+    if qw.shape[1] != kb or sx.shape[0] != b or sw.shape[0] != n:
+        raise ValueError("inconsistent shapes of qx/sx/qw/sw")
+    r = 0
+    if l2t is not None or t is not None:
+        _need(t, "t", torch.float32, 2)
+        _need(l2t, "l2t", torch.float16, 2)
+        r = l2t.shape[1]
+        if t.shape != (b, r) or l2t.shape[0] != n:
+            raise ValueError("t must be [b][r] and l2t [n][r]")
+    dev = qx.device
+    for name, ten in (("sx", sx), ("qw", qw), ("sw", sw), ("t", t), ("l2t", l2t)):
+        if ten is not None and ten.device != dev:
+            raise ValueError(f"{name} is on {ten.device}, qx on {dev}")
+    y = out if out is not None else torch.empty((b, n), dtype=torch.float16, device=dev)
+    _need(y, "out", torch.float16, 2)
+    if y.shape != (b, n):
+        raise ValueError("out must be [b][n]")
+    _check(lib().twq_dual_linear(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(t), _ptr(l2t), r,
+                                 _ptr(y), b, m, n, _stream(dev)), "twq_dual_linear")
+    return y
+
+
+def debug_residual_acc(qx, qw):
+    """int32 [b][n] = Q_X . Q_W^T computed by the fused kernel's main loop."""
+    _need(qx, "qx", torch.uint8, 2)
+    _need(qw, "qw", torch.uint8, 2)
+    b, kb = qx.shape
+    n = qw.shape[0]
+    acc = torch.empty((b, n), dtype=torch.int32, device=qx.device)
+    _check(lib().twq_debug_residual_acc(_ptr(qx), _ptr(qw), _ptr(acc), b, 2 * kb, n,
+                                        _stream(qx.device)), "twq_debug_residual_acc")
+    return acc
+
+
+class DualLinear:
+    """A packed layer: Q_W, s_W and the fp16 low-rank pair, resident on one GPU."""
+
+    def __init__(self, w_res: torch.Tensor, l1t: torch.Tensor | None, l2t: torch.Tensor | None):
+        self.qw, self.sw = pack_weight(w_res)
+        self.l1t = l1t
+        self.l2t = l2t
+        self.n, self.m = w_res.shape
+        self.r = 0 if l1t is None else l1t.shape[0]
+
+    def __call__(self, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+        qx, sx, t = quantize_act(x, self.l1t if self.r else None)
+        return dual_linear(qx, sx, self.qw, self.sw, t, self.l2t if self.r else None, out=out)

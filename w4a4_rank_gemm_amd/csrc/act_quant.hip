@@ -1,0 +1,352 @@
+// act_quant.hip -- activation side of the fused W4A4 + low-rank linear (gfx950).
+//
+// One launch does two independent jobs that both only read X:
+//  * per-token quantization (TwinQuant page 1, section 2, eq. (1)): a CTA of 256
+//    threads computes amax over a token row with a wave reduction, s_X =
+//    amax / 7, and the packed 4-bit codes of its slice of the row (few tokens:
+//    several CTAs per row); short rows stay in registers between the two passes,
+//    long rows are re-read from cache;
+//  * the first low-rank product T = X L1 of eq. (3) on fp16 matrix cores with
+//    fp32 accumulation, cut into K slices so the read of X and L1 is spread over
+//    many compute units (one unit streams only tens of GB/s from HBM). A second,
+//    elementwise kernel adds the slices' partial sums in slice order. Every sum
+//    has a fixed order, so T is bitwise reproducible.
+// The T CTAs take the low block indices so the longer jobs start first.
+#include "twq_device.h"
+#include "twq_kernels.h"
+
+namespace twq {
+
+constexpr int kActThreads = 256;
+constexpr int kActMaxJ = 8;   // rows of up to 256 * 8 * 8 = 16384 fp16 stay in registers
+
+struct ActDev {
+    int mode;        // 0: tiles of 64 token rows x all ranks; 1: all tokens x 16 ranks x a K slice
+    int row_tile, ks, row_tiles, n_t_ctas;
+    int fm;          // mode 1: token tiles of 16 (b <= 128)
+    int nsl;         // CTAs per token row for the quantizer
+};
+
+__device__ __forceinline__ uint32_t absmax8_bits(const uint4 c, uint32_t mx) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // |x| of an fp16 is its bit pattern without the sign; for finite values the
+        // integer order of these patterns is the order of the magnitudes
+        uint32_t lo = w[e] & 0x7FFFu, hi = (w[e] >> 16) & 0x7FFFu;
+        mx = mx > lo ? mx : lo;
+        mx = mx > hi ? mx : hi;
+    }
+    return mx;
+}
+
+__device__ __forceinline__ uint32_t quant8(const uint4 c, float s) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    int q[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        q[2 * e] = quant_code(half_bits_to_float(w[e] & 0xFFFFu), s);
+        q[2 * e + 1] = quant_code(half_bits_to_float(w[e] >> 16), s);
+    }
+    return pack8(q);
+}
+
+// Slice sl (of nsl) of one token row, by one CTA of 256 threads: amax is taken over
+// the whole row (every slice reads it; only the first reads it from HBM), the codes
+// are written for the slice's chunks only. Spreading a short row over several
+// CTAs spreads its divisions over several compute units.
+__device__ void quantize_row(const ActArgs &a, int64_t i, int sl, int nsl, uint32_t *red) {
+    const int tid = threadIdx.x;
+    const int64_t nch = a.m / 8;  // 16-byte chunks of 8 fp16
+    const int64_t c_lo = nch * sl / nsl, c_hi = nch * (sl + 1) / nsl;
+    const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + i * a.m);
+    uint32_t *qr = reinterpret_cast<uint32_t *>(a.qx + i * (a.m / 2));
+    const bool cached = nch <= (int64_t)kActThreads * kActMaxJ;
+    uint4 v[kActMaxJ];
+    uint32_t mx = 0;
+    if (cached) {
+#pragma unroll
+        for (int j = 0; j < kActMaxJ; ++j) {
+            const int64_t c = tid + (int64_t)j * kActThreads;
+            v[j] = c < nch ? xr[c] : make_uint4(0, 0, 0, 0);
+            mx = absmax8_bits(v[j], mx);
+        }
+    } else {
+        for (int64_t c = tid; c < nch; c += kActThreads) mx = absmax8_bits(xr[c], mx);
+    }
+    mx = wave_max_u32(mx);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = mx;
+    __syncthreads();
+    mx = red[0];
+#pragma unroll
+    for (int w = 1; w < kActThreads / kWave; ++w) mx = mx > red[w] ? mx : red[w];
+    const float amax = half_bits_to_float(mx);
+    const float s = amax / kQMax;  // correctly rounded binary32 division
+    if (tid == 0 && sl == 0) a.sx[i] = s;
+    if (cached) {
+#pragma unroll
+        for (int j = 0; j < kActMaxJ; ++j) {
+            const int64_t c = tid + (int64_t)j * kActThreads;
+            if (c >= c_lo && c < c_hi) qr[c] = amax == 0.0f ? 0u : quant8(v[j], s);
+        }
+    } else {
+        for (int64_t c = c_lo + tid; c < c_hi; c += kActThreads) qr[c] = amax == 0.0f ? 0u : quant8(xr[c], s);
+    }
+}
+
+// T tile for many tokens: rows [64 rt, 64 rt + 64) (one 16-row slab per wave) x all
+// r = 16 NT ranks, over K slice ks. A = L1^T rows (16 ranks), B = X rows (16
+// tokens), so lane (li, g) ends with ranks 4g..4g+3 of token li in each rank tile.
+// U steps of 32 are loaded before any is multiplied. With several K slices the
+// partial sums go to partials[ks] and a second kernel adds them in slice order.
+template <int NT>
+__device__ void t_rows(const ActArgs &a, const ActDev &p, int tb) {
+    constexpr int U = NT <= 4 ? 4 : (NT <= 8 ? 2 : 1);
+    const int rt = tb / p.ks, ks = tb % p.ks;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int li = lane & 15, g = lane >> 4;
+    const int64_t kslice = a.m / p.ks;
+    const int64_t kbeg = ks * kslice, kend = kbeg + kslice;
+    const int64_t row = (int64_t)rt * 64 + wave * 16 + li;
+    const bool rv = row < a.b;
+    const uint16_t *xp = a.x + (rv ? row : 0) * a.m + g * 8;
+    const uint16_t *lp = a.l1t + (int64_t)li * a.m + g * 8;
+
+    v4f acc[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int64_t k = kbeg; k < kend; k += 32 * U) {
+        v8h xb[U], la[U][NT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kk = k + 32 * u;
+            const bool ok = kk < kend;
+            xb[u] = (ok && rv) ? load_h8(xp + kk) : v8h{};
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) la[u][tt] = ok ? load_h8(lp + (int64_t)tt * 16 * a.m + kk) : v8h{};
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load of the batch in flight before the first use
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma_f16(la[u][tt], xb[u], acc[tt]);
+    }
+    if (p.ks == 1) {
+        if (rv) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) *reinterpret_cast<v4f *>(a.t + row * a.r + tt * 16 + 4 * g) = acc[tt];
+        }
+        return;
+    }
+    const int64_t prow_stride = (int64_t)p.row_tiles * 64 * a.r;
+    float *dst = a.partials + ks * prow_stride + row * a.r + 4 * g;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) *reinterpret_cast<v4f *>(dst + tt * 16) = acc[tt];
+}
+
+// T partial for few tokens: all b tokens (FM tiles of 16) x ranks [16 rt, 16 rt + 16)
+// over K slice ks, written to partials[ks]; the four waves split the slice and are
+// added through LDS in wave order. A = L1^T rows (16 ranks), B = X rows (16 tokens):
+// lane (li, g) ends with ranks 4g..4g+3 of token li of each token tile.
+template <int FM>
+__device__ void t_slices(const ActArgs &a, const ActDev &p, int tb, float *lds) {
+    constexpr int U = FM <= 2 ? 4 : 2;
+    const int rt = tb % p.row_tiles, ks = tb / p.row_tiles;  // row_tiles = r / 16 rank tiles
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int li = lane & 15, g = lane >> 4;
+    const int64_t nsteps = a.m / 32;
+    const int64_t s_lo = nsteps * ks / p.ks, s_hi = nsteps * (ks + 1) / p.ks;
+    const int64_t sb = s_lo + (s_hi - s_lo) * wave / 4, se = s_lo + (s_hi - s_lo) * (wave + 1) / 4;
+    const uint16_t *lp = a.l1t + ((int64_t)rt * 16 + li) * a.m + g * 8;
+    const uint16_t *xp[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int64_t tok = fm * 16 + li;
+        xp[fm] = a.x + (tok < a.b ? tok : a.b - 1) * a.m + g * 8;  // rows past b: never stored
+    }
+    v4f acc[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) acc[fm] = v4f{0.f, 0.f, 0.f, 0.f};
+    int64_t st = sb;
+    for (; st + U <= se; st += U) {
+        v8h la[U], xb[U][FM];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            la[u] = load_h8(lp + (st + u) * 32);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) xb[u][fm] = load_h8(xp[fm] + (st + u) * 32);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load of the batch in flight before the first use
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) acc[fm] = mfma_f16(la[u], xb[u][fm], acc[fm]);
+    }
+    for (; st < se; ++st) {
+        const v8h la = load_h8(lp + st * 32);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) acc[fm] = mfma_f16(la, load_h8(xp[fm] + st * 32), acc[fm]);
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            *reinterpret_cast<v4f *>(lds + (((wave - 1) * FM + fm) * kWave + lane) * 4) = acc[fm];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 1; w < 4; ++w)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) acc[fm] += *reinterpret_cast<const v4f *>(lds + (((w - 1) * FM + fm) * kWave + lane) * 4);
+    const int64_t rank = (int64_t)rt * 16 + 4 * g;
+    const int64_t tpad = (int64_t)FM * 16;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        float *dst = p.ks == 1 ? a.t + (fm * 16 + li) * (int64_t)a.r + rank
+                               : a.partials + (ks * tpad + fm * 16 + li) * a.r + rank;
+        if (p.ks > 1 || fm * 16 + li < a.b) *reinterpret_cast<v4f *>(dst) = acc[fm];
+    }
+}
+
+// Many tokens (MODE 0): T partials by t_rows<NT>. Few tokens (MODE 1): T partials by
+// t_slices<NT = FM>. The remaining CTAs quantize, nsl CTAs per token row.
+template <int MODE, int NT>
+__global__ __launch_bounds__(kActThreads) void act_kernel(ActArgs a, ActDev p) {
+    __shared__ float lds[MODE == 1 ? 3 * NT * kWave * 4 : 1];
+    __shared__ uint32_t red[kActThreads / kWave];
+    const int64_t bid = blockIdx.x;
+    if (bid < p.n_t_ctas) {
+        if constexpr (MODE == 0)
+            t_rows<NT>(a, p, (int)bid);
+        else
+            t_slices<NT>(a, p, (int)bid, lds);
+    } else {
+        const int64_t q = bid - p.n_t_ctas;
+        quantize_row(a, q / p.nsl, (int)(q % p.nsl), p.nsl, red);
+    }
+}
+
+// T[row][c] = sum over slices s (in slice order) of partials[s][row][c]. Loads are
+// issued eight slices at a time before any is added.
+__global__ __launch_bounds__(256) void t_reduce_kernel(const float *partials, int64_t b, int64_t rows_pad,
+                                                       int r, int ks, float *t) {
+    const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 index into T
+    const int64_t n4 = b * r / 4;
+    if (i4 >= n4) return;
+    const int64_t stride = rows_pad * r;
+    const float *src = partials + i4 * 4;
+    v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ks; s0 += 8) {
+        v4f v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < ks) v[u] = *reinterpret_cast<const v4f *>(src + (s0 + u) * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < ks) sum += v[u];
+    }
+    *reinterpret_cast<v4f *>(t + i4 * 4) = sum;
+}
+
+static int64_t pow2_floor(int64_t v) {
+    int64_t p = 1;
+    while (p * 2 <= v) p *= 2;
+    return p;
+}
+
+ActPlan plan_act(int64_t b, int64_t m, int64_t r) {
+    ActPlan pl{};
+    pl.ks = 1;
+    pl.nsl = 1;
+    if (b == 0) return pl;
+    if (b > 128) {
+        // many tokens: 64-row tiles x all ranks; K slices until about 512 CTAs,
+        // keeping slices of at least 512
+        pl.mode = 0;
+        pl.row_tile = 64;
+        pl.row_tiles = (int)((b + 63) / 64);
+        int64_t ks = 1;
+        if (r > 0)
+            while ((int64_t)pl.row_tiles * ks < 512 && m / (ks * 2) >= 512 && m % (ks * 2 * 32) == 0) ks *= 2;
+        pl.ks = (int)ks;
+    } else {
+        // few tokens: every token x one 16-rank tile x one K slice per CTA, slices of
+        // about 16 KB of X and L1 each (a compute unit streams only tens of GB/s, so
+        // the read is spread wide); each short token row is quantized by nsl CTAs
+        pl.mode = 1;
+        pl.fm = (int)((b + 15) / 16);
+        pl.row_tile = pl.fm * 16;
+        pl.row_tiles = (int)(r / 16);
+        const int64_t bytes = m * (16 * pl.fm + 16) * 2;
+        int64_t ks = pow2_floor(bytes / 16384 > 0 ? bytes / 16384 : 1);
+        const int64_t max_ks = m / 128 < 32 ? m / 128 : 32;  // each wave keeps at least one step
+        while (ks > max_ks) ks /= 2;
+        pl.ks = r > 0 ? (int)ks : 1;
+        int64_t nsl = 1;
+        while (b * nsl < 128 && (m / 8) / (nsl * 2) >= 32) nsl *= 2;
+        pl.nsl = (int)nsl;
+    }
+    if (r > 0 && pl.ks > 1) {
+        const int64_t rows_pad = pl.mode == 0 ? (int64_t)pl.row_tiles * 64 : (int64_t)pl.fm * 16;
+        pl.workspace_bytes = (size_t)pl.ks * rows_pad * r * sizeof(float);
+    }
+    return pl;
+}
+
+template <int MODE, int NT>
+static void launch_one(const ActArgs &a, const ActDev &p, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((act_kernel<MODE, NT>), dim3((unsigned)grid), dim3(kActThreads), 0, stream, a, p);
+}
+
+template <int MODE>
+static bool launch_nt(int nt, const ActArgs &a, const ActDev &p, int64_t grid, hipStream_t s) {
+    switch (nt) {
+        case 0: case 1: launch_one<MODE, 1>(a, p, grid, s); return true;
+        case 2: launch_one<MODE, 2>(a, p, grid, s); return true;
+        case 3: launch_one<MODE, 3>(a, p, grid, s); return true;
+        case 4: launch_one<MODE, 4>(a, p, grid, s); return true;
+        case 5: launch_one<MODE, 5>(a, p, grid, s); return true;
+        case 6: launch_one<MODE, 6>(a, p, grid, s); return true;
+        case 7: launch_one<MODE, 7>(a, p, grid, s); return true;
+        case 8: launch_one<MODE, 8>(a, p, grid, s); return true;
+        default: break;
+    }
+    if constexpr (MODE == 0) {
+        switch (nt) {
+            case 9: launch_one<0, 9>(a, p, grid, s); return true;
+            case 10: launch_one<0, 10>(a, p, grid, s); return true;
+            case 11: launch_one<0, 11>(a, p, grid, s); return true;
+            case 12: launch_one<0, 12>(a, p, grid, s); return true;
+            case 13: launch_one<0, 13>(a, p, grid, s); return true;
+            case 14: launch_one<0, 14>(a, p, grid, s); return true;
+            case 15: launch_one<0, 15>(a, p, grid, s); return true;
+            case 16: launch_one<0, 16>(a, p, grid, s); return true;
+            default: break;
+        }
+    }
+    return false;
+}
+
+hipError_t launch_act(const ActArgs &a, const ActPlan &pl, hipStream_t stream) {
+    if (a.b == 0) return hipSuccess;
+    ActDev p{};
+    p.mode = pl.mode;
+    p.fm = pl.fm;
+    p.row_tile = pl.row_tile;
+    p.ks = pl.ks;
+    p.row_tiles = pl.row_tiles;
+    p.nsl = pl.nsl;
+    p.n_t_ctas = a.r > 0 ? pl.row_tiles * pl.ks : 0;
+    const int64_t grid = p.n_t_ctas + a.b * pl.nsl;
+    const bool ok = pl.mode == 0 ? launch_nt<0>(a.r / 16, a, p, grid, stream)
+                                 : launch_nt<1>(a.r > 0 ? pl.fm : 1, a, p, grid, stream);
+    if (!ok) return hipErrorInvalidValue;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.r == 0 || pl.ks == 1) return e;
+    const int64_t n4 = a.b * a.r / 4;
+    const int64_t rows_pad = pl.mode == 0 ? (int64_t)pl.row_tiles * 64 : (int64_t)pl.fm * 16;
+    hipLaunchKernelGGL(t_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a.partials, a.b,
+                       rows_pad, a.r, pl.ks, a.t);
+    return hipGetLastError();
+}
+
+}  // namespace twq

@@ -1,0 +1,138 @@
+// twq_api.cpp -- the C ABI of libtwq: argument validation, planning and launches.
+// Every check happens before the first HIP call, so a rejected call launches nothing.
+#include "twq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "twq_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+twq_status hip_fail(hipError_t e, const char *where) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+    return TWQ_ERR_HIP;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxM = 131072;    // keeps 256 * 49 * m below 2^31 in the int32 accumulator
+constexpr int64_t kMaxTokens = int64_t(1) << 24;
+constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr int64_t kMaxRank = 256;
+
+bool valid_m(int64_t m) { return m > 0 && m % 128 == 0 && m <= kMaxM; }
+bool valid_b(int64_t b) { return b >= 0 && b <= kMaxTokens; }
+bool valid_n(int64_t n) { return n >= 0 && n % 16 == 0 && n <= kMaxN; }
+bool valid_r(int64_t r) { return r >= 0 && r % 16 == 0 && r <= kMaxRank; }
+
+}  // namespace
+
+extern "C" {
+
+const char *twq_status_string(int status) {
+    switch (status) {
+        case TWQ_OK: return "ok";
+        case TWQ_ERR_NULL: return "null pointer";
+        case TWQ_ERR_SHAPE: return "unsupported shape";
+        case TWQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case TWQ_ERR_UNSUPPORTED: return "unsupported argument combination";
+        case TWQ_ERR_HIP: return "HIP runtime error";
+        case TWQ_ERR_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+const char *twq_last_error_string(void) { return g_last_error; }
+
+int twq_version(void) { return 100; }
+
+size_t twq_quantize_act_workspace_bytes(int64_t b, int64_t m, int64_t r) {
+    if (!valid_b(b) || !valid_m(m) || !valid_r(r)) return 0;
+    return twq::plan_act(b, m, r).workspace_bytes;
+}
+
+twq_status twq_quantize_act(const void *x, int64_t b, int64_t m, void *qx, float *sx, const void *l1t,
+                            int64_t r, float *t, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!valid_b(b) || !valid_m(m) || !valid_r(r)) return TWQ_ERR_SHAPE;
+    if (b == 0) return TWQ_OK;
+    if (!x || !qx || !sx) return TWQ_ERR_NULL;
+    if (r > 0 && (!l1t || !t)) return TWQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(qx) || !aligned16(sx)) return TWQ_ERR_ALIGN;
+    if (r > 0 && (!aligned16(l1t) || !aligned16(t))) return TWQ_ERR_ALIGN;
+    const twq::ActPlan plan = twq::plan_act(b, m, r);
+    if (r > 0 && plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.workspace_bytes) return TWQ_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return TWQ_ERR_ALIGN;
+    }
+    twq::ActArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.b = b;
+    a.m = m;
+    a.qx = static_cast<uint8_t *>(qx);
+    a.sx = sx;
+    a.l1t = static_cast<const uint16_t *>(l1t);
+    a.r = (int)r;
+    a.t = t;
+    if (r > 0 && plan.workspace_bytes > 0) a.partials = static_cast<float *>(workspace);
+    const hipError_t e = twq::launch_act(a, plan, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_quantize_act");
+}
+
+twq_status twq_pack_weight(const float *w_res, int64_t n, int64_t m, void *qw, float *sw, void *stream) {
+    if (!valid_n(n) || !valid_m(m)) return TWQ_ERR_SHAPE;
+    if (n == 0) return TWQ_OK;
+    if (!w_res || !qw || !sw) return TWQ_ERR_NULL;
+    if (!aligned16(w_res) || !aligned16(qw) || !aligned16(sw)) return TWQ_ERR_ALIGN;
+    const hipError_t e = twq::launch_pack_weight(w_res, n, m, static_cast<uint8_t *>(qw), sw,
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_pack_weight");
+}
+
+twq_status twq_dual_linear(const void *qx, const float *sx, const void *qw, const float *sw, const float *t,
+                           const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n, void *stream) {
+    if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return TWQ_ERR_SHAPE;
+    if (b == 0 || n == 0) return TWQ_OK;
+    if (!qx || !sx || !qw || !sw || !y) return TWQ_ERR_NULL;
+    if (r > 0 && (!t || !l2t)) return TWQ_ERR_NULL;
+    if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(sw) || !aligned16(y))
+        return TWQ_ERR_ALIGN;
+    if (r > 0 && (!aligned16(t) || !aligned16(l2t))) return TWQ_ERR_ALIGN;
+    twq::DualArgs a{};
+    a.qx = static_cast<const uint8_t *>(qx);
+    a.sx = sx;
+    a.qw = static_cast<const uint8_t *>(qw);
+    a.sw = sw;
+    a.t = t;
+    a.l2t = static_cast<const uint16_t *>(l2t);
+    a.r = (int)r;
+    a.y = static_cast<uint16_t *>(y);
+    a.b = b;
+    a.m = m;
+    a.n = n;
+    const hipError_t e = twq::launch_dual_linear(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_dual_linear");
+}
+
+twq_status twq_debug_residual_acc(const void *qx, const void *qw, int32_t *acc, int64_t b, int64_t m, int64_t n,
+                                  void *stream) {
+    if (!valid_b(b) || !valid_m(m) || !valid_n(n)) return TWQ_ERR_SHAPE;
+    if (b == 0 || n == 0) return TWQ_OK;
+    if (!qx || !qw || !acc) return TWQ_ERR_NULL;
+    if (!aligned16(qx) || !aligned16(qw) || !aligned16(acc)) return TWQ_ERR_ALIGN;
+    twq::DualArgs a{};
+    a.qx = static_cast<const uint8_t *>(qx);
+    a.qw = static_cast<const uint8_t *>(qw);
+    a.acc = acc;
+    a.b = b;
+    a.m = m;
+    a.n = n;
+    const hipError_t e = twq::launch_dual_linear(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_debug_residual_acc");
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// twq_kernels.h -- launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace twq {
+
+// ---- activation quantizer + first low-rank product ------------------------------
+
+// How the activation launch is split. T = X L1 is cut into ks K slices whose partial
+// sums (in the workspace) a second kernel adds. Many tokens (mode 0): tiles of 64
+// token rows x all ranks, one 16-row slab per wave. Few tokens (mode 1): every
+// token x one 16-rank tile per CTA, the four waves splitting the CTA's slice. The
+// quantizer takes nsl CTAs per token row.
+struct ActPlan {
+    int mode;        // 0 or 1, as above
+    int fm;          // mode 1: token tiles of 16
+    int row_tile;    // token rows of the partial-sum layout per tile: 64 (mode 0) or 16 fm (mode 1)
+    int ks;          // K slices; 1 means T is written directly
+    int row_tiles;   // mode 0: ceil(b / 64) row tiles; mode 1: r / 16 rank tiles
+    int nsl;         // CTAs per token row for the quantizer
+    size_t workspace_bytes;  // partial sums of T: ks slices of [row_tiles * 64 or 16 fm][r] floats
+};
+
+ActPlan plan_act(int64_t b, int64_t m, int64_t r);
+
+struct ActArgs {
+    const uint16_t *x;
+    int64_t b, m;
+    uint8_t *qx;
+    float *sx;
+    const uint16_t *l1t;
+    int r;
+    float *t;
+    float *partials;  // ks > 1: [ks][rows_pad][r], rows_pad = 64 row_tiles (mode 0) or 16 fm (mode 1)
+};
+
+hipError_t launch_act(const ActArgs &a, const ActPlan &plan, hipStream_t stream);
+// ---- weight packer -----------------------------------------------------------------
+
+hipError_t launch_pack_weight(const float *w, int64_t n, int64_t m, uint8_t *qw, float *sw,
+                              hipStream_t stream);
+
+// ---- fused dual linear ----------------------------------------------------------------
+
+struct DualArgs {
+    const uint8_t *qx;
+    const float *sx;
+    const uint8_t *qw;
+    const float *sw;
+    const float *t;
+    const uint16_t *l2t;
+    int r;
+    uint16_t *y;       // fp16 [b][n]
+    int32_t *acc;      // debug: int32 [b][n] instead of y
+    int64_t b, m, n;
+};
+
+hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream);
+
+}  // namespace twq
