@@ -130,6 +130,54 @@ twq_status twq_dual_linear(const void *qx, const float *sx, const void *qw, cons
 twq_status twq_debug_residual_acc(const void *qx, const void *qw, int32_t *acc, int64_t b,
                                   int64_t m, int64_t n, void *stream);
 
+/*
+ * ---- int4 low-rank variant (TwinQuant page 1, section 4.3) ----
+ *
+ * Both low-rank factors in 4 bits: the first low-rank GEMM gives INT32 H = Q_X Q_L1,
+ * which gets a scale s_H from the accumulators and is requantized to packed 4-bit
+ * Q_H for the second GEMM; one epilogue merges both branches:
+ *
+ *   Y[i][j] = fp16( s_X[i] s_W[j] (Q_X Q_W^T)[i][j] + s_H[i] (Q_H Q_L2^T)[i][j] )
+ *
+ * Readings: L1 (m x r) is quantized with one scale per column t and L2 (r x n) with
+ * one per row t (eq. (1) each); s_L2[t] cannot stay inside the integer sum over t,
+ * so both factor scales fold into H before requantization: h[i][t] =
+ * (s_X[i] H[i][t]) c[t], c[t] = s_L1[t] s_L2[t], binary32 in that order; s_H[i] =
+ * max_t |h[i][t]| / 7 (one scale per token), Q_H = round(h / s_H) by eq. (1).
+ * Ranks: r = 0 or a multiple of 32 up to 256.
+ */
+
+/*
+ *   l1t   fp16 [r][m], l2t fp16 [n][r]   as for twq_quantize_act / twq_dual_linear
+ *   ql1   u8  [r][m/2]  (out)            codes of L1 per rank t (row t = column t of L1)
+ *   sl1   f32 [r]       (out)            s_L1[t] = max_k |L1[k][t]| / 7
+ *   ql2   u8  [n][r/2]  (out)            codes of L2, K = r contiguous per output channel
+ *   sl2   f32 [r]       (out)            s_L2[t] = max_j |L2[t][j]| / 7
+ *   c     f32 [r]       (out)            c[t] = s_L1[t] s_L2[t]
+ */
+twq_status twq_pack_lowrank_int4(const void *l1t, const void *l2t, int64_t r, int64_t m, int64_t n,
+                                 void *ql1, float *sl1, void *ql2, float *sl2, float *c, void *stream);
+
+/*
+ * H = Q_X Q_L1^T and its requantization, once per call.
+ *   qx, sx     from twq_quantize_act;  ql1, c  from twq_pack_lowrank_int4
+ *   h     i32 [b][r]    (out)          the exact integer H
+ *   qh    u8  [b][r/2]  (out)          packed Q_H
+ *   sh    f32 [b]       (out)          s_H per token
+ */
+twq_status twq_lowrank_requant(const void *qx, const float *sx, const void *ql1, const float *c,
+                               int64_t r, int32_t *h, void *qh, float *sh, int64_t b, int64_t m,
+                               void *stream);
+
+/*
+ * The fused layer with the int4 low-rank branch (see above); qh, sh from
+ * twq_lowrank_requant, ql2 from twq_pack_lowrank_int4; qh, sh, ql2 may be NULL
+ * when r == 0.
+ */
+twq_status twq_dual_linear_lr4(const void *qx, const float *sx, const void *qw, const float *sw,
+                               const void *qh, const float *sh, const void *ql2, int64_t r,
+                               void *y, int64_t b, int64_t m, int64_t n, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

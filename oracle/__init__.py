@@ -59,6 +59,8 @@ def _load():
         lib.orc_lowrank_requant.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P]
         lib.orc_dual_linear_lr4.restype = ctypes.c_int
         lib.orc_dual_linear_lr4.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P]
+        lib.orc_dual_linear_lr4_sampled.restype = ctypes.c_int
+        lib.orc_dual_linear_lr4_sampled.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P]
         lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -238,6 +240,28 @@ def dual_linear_lr4(x, w_res, l1t, l2t):
     if rc:
         raise MemoryError("oracle allocation failed")
     return out
+
+
+def dual_linear_lr4_sampled(x, w_res, l1t, l2t, rows, cols):
+    """The int4 low-rank layer at the positions (rows[p], cols[p]): (acc, acc2, y)."""
+    xb = _h(x)
+    w = _c(w_res, np.float32)
+    b, m = xb.shape
+    n = w.shape[0]
+    l1, l2 = _h(l1t), _h(l2t)
+    r = l1.shape[0]
+    rows = _c(rows, np.int64)
+    cols = _c(cols, np.int64)
+    assert rows.shape == cols.shape and rows.ndim == 1
+    assert ((0 <= rows) & (rows < b)).all() and ((0 <= cols) & (cols < n)).all()
+    acc = np.empty(rows.shape[0], np.int64)
+    acc2 = np.empty(rows.shape[0], np.int64)
+    y = np.empty(rows.shape[0], np.float64)
+    rc = _load().orc_dual_linear_lr4_sampled(_p(xb), _p(w), _p(l1), _p(l2), b, m, n, r, _p(rows), _p(cols),
+                                             rows.shape[0], _p(acc), _p(acc2), _p(y))
+    if rc:
+        raise MemoryError("oracle allocation failed")
+    return acc, acc2, y
 
 
 def unpack_codes(packed):

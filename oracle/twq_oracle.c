@@ -368,6 +368,56 @@ int orc_dual_linear_lr4(const uint16_t *x, const float *w_res, const uint16_t *l
     return 0;
 }
 
+/* The int4 low-rank layer at sampled positions (rows[p], cols[p]) only, from the same
+ * definition as orc_dual_linear_lr4: the factors are quantized whole (they are small),
+ * H and Q_H are formed for the sampled tokens, acc and acc2 at the sampled outputs. */
+int orc_dual_linear_lr4_sampled(const uint16_t *x, const float *w_res, const uint16_t *l1t,
+                                const uint16_t *l2t, int64_t b, int64_t m, int64_t n, int64_t r,
+                                const int64_t *rows, const int64_t *cols, int64_t count,
+                                int64_t *acc_out, int64_t *acc2_out, double *y_out)
+{
+    (void)b;
+    int8_t *ql1 = (int8_t *)malloc((size_t)(r * m));
+    int8_t *ql2 = (int8_t *)malloc((size_t)(n * r));
+    float *sl1 = (float *)malloc(sizeof(float) * (size_t)r);
+    float *sl2 = (float *)malloc(sizeof(float) * (size_t)r);
+    float *c = (float *)malloc(sizeof(float) * (size_t)r);
+    if (!ql1 || !ql2 || !sl1 || !sl2 || !c)
+        return 1;
+    if (orc_quantize_lowrank(l1t, l2t, r, m, n, ql1, NULL, sl1, ql2, NULL, sl2, c))
+        return 1;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < count; p++) {
+        int64_t i = rows[p], j = cols[p];
+        float *xr = (float *)malloc(sizeof(float) * (size_t)m);
+        int8_t *qx = (int8_t *)malloc((size_t)m);
+        int8_t *qw = (int8_t *)malloc((size_t)m);
+        int8_t *qh = (int8_t *)malloc((size_t)(r > 0 ? r : 1));
+        if (!xr || !qx || !qw || !qh) {
+            fail = 1;
+            continue;
+        }
+        float sxi, swj, shi;
+        for (int64_t k = 0; k < m; k++)
+            xr[k] = (float)orc_half_to_double(x[i * m + k]);
+        quantize_vector(xr, m, qx, &sxi);
+        quantize_vector(w_res + j * m, m, qw, &swj);
+        orc_lowrank_requant(qx, &sxi, ql1, c, 1, m, r, qh, NULL, &shi, NULL);
+        int64_t acc = 0, acc2 = 0;
+        for (int64_t k = 0; k < m; k++)
+            acc += (int64_t)qx[k] * (int64_t)qw[k];
+        for (int64_t t = 0; t < r; t++)
+            acc2 += (int64_t)qh[t] * (int64_t)ql2[j * r + t];
+        acc_out[p] = acc;
+        acc2_out[p] = acc2;
+        y_out[p] = (double)sxi * (double)swj * (double)acc + (double)shi * (double)acc2;
+        free(xr); free(qx); free(qw); free(qh);
+    }
+    free(ql1); free(ql2); free(sl1); free(sl2); free(c);
+    return fail;
+}
+
 #ifdef _OPENMP
 #include <omp.h>
 #endif

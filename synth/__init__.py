@@ -141,6 +141,8 @@ def split_lowrank(w_nm: np.ndarray, r: int, method: str, rng=None):
 
     Returns (l1t fp16 [r][m], l2t fp16 [n][r], w_res fp32 [n][m])."""
     n, m = w_nm.shape
+    if r > min(n, m):
+        raise ValueError(f"rank {r} exceeds min(n, m) = {min(n, m)}: the split has no such component")
     if r == 0:
         return (np.zeros((0, m), np.float16), np.zeros((n, 0), np.float16),
                 w_nm.astype(np.float32))

@@ -95,3 +95,19 @@ def test_binding_fails_loudly_without_gpu_tensors():
     x = torch.zeros(4, 256, dtype=torch.float16)
     with pytest.raises(ValueError):
         twq.quantize_act(x)
+
+
+def test_lowrank_int4_validation():
+    L = twq.lib()
+    # ranks must be a multiple of 32 for the int4 low-rank variant
+    assert L.twq_pack_lowrank_int4(A, A, 16, 256, 32, A, A, A, A, A, None) == SHAPE
+    assert L.twq_lowrank_requant(A, A, A, A, 48, A, A, A, 4, 256, None) == SHAPE
+    assert L.twq_dual_linear_lr4(A, A, A, A, A, A, A, 16, A, 4, 256, 32, None) == SHAPE
+    assert L.twq_pack_lowrank_int4(None, A, 32, 256, 32, A, A, A, A, A, None) == NULL
+    assert L.twq_lowrank_requant(A, A, A, A, 32, None, A, A, 4, 256, None) == NULL
+    assert L.twq_dual_linear_lr4(A, A, A, A, None, A, A, 32, A, 4, 256, 32, None) == NULL
+    assert L.twq_dual_linear_lr4(A, A, A, A, A, A, MIS, 32, A, 4, 256, 32, None) == ALIGN
+    # empty calls
+    assert L.twq_pack_lowrank_int4(None, None, 0, 256, 32, None, None, None, None, None, None) == OK
+    assert L.twq_lowrank_requant(None, None, None, None, 32, None, None, None, 0, 256, None) == OK
+    assert L.twq_dual_linear_lr4(None, None, None, None, None, None, None, 32, None, 0, 256, 32, None) == OK

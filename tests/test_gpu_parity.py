@@ -125,8 +125,10 @@ def test_config_full(name):
 # channel tile, m with a half stage, r not a multiple of 32, rank 0, largest rank
 RAGGED = [
     (1, 128, 16, 16), (17, 384, 48, 32), (33, 512, 80, 48), (130, 640, 144, 16),
-    (5, 256, 272, 0), (64, 1024, 128, 128), (200, 256, 64, 256), (2, 4096, 32, 32),
-    (129, 1152, 208, 64), (16, 256, 16, 240),
+    (5, 256, 272, 0), (64, 1024, 128, 128), (200, 256, 272, 256), (2, 4096, 32, 32),
+    (129, 1152, 208, 64), (16, 256, 256, 240),
+    # few-token launch shapes whose CTAs own more output tiles than waves
+    (32, 1024, 8192, 64), (64, 512, 8192, 32), (16, 512, 16384, 16), (27, 512, 8208, 48),
 ]
 
 
@@ -172,7 +174,7 @@ def test_repeat_runs_bitwise_equal():
 def test_workspace_shared_across_shapes():
     """Calls of different shapes share one workspace: many-token calls with K slices
     (partial sums in the workspace) interleaved with few-token calls."""
-    for b, m, n, r in [(129, 1152, 208, 64), (3, 8192, 16, 16), (300, 2048, 64, 32), (17, 4096, 32, 48)]:
+    for b, m, n, r in [(129, 1152, 208, 64), (3, 8192, 16, 16), (300, 2048, 64, 32), (17, 4096, 64, 48)]:
         _say(f"shape b={b} m={m} n={n} r={r}")
         d = synth.make_random(b, m, n, r, seed=b + m)
         check_full(d, run_gpu(d))

@@ -359,6 +359,19 @@ def test_lr4_rank1_identity(oracle_lib):
     np.testing.assert_allclose(out["y"], exact, rtol=4e-7, atol=0)
 
 
+def test_lr4_sampled_matches_full(oracle_lib):
+    d = synth.make_random(12, 256, 48, 32, seed=21)
+    full = oracle_lib.dual_linear_lr4(d["x"], d["w_res"], d["l1t"], d["l2t"])
+    rng = synth.rng_for(22)
+    rows = rng.integers(0, 12, 40)
+    cols = rng.integers(0, 48, 40)
+    acc, acc2, y = oracle_lib.dual_linear_lr4_sampled(d["x"], d["w_res"], d["l1t"], d["l2t"], rows, cols)
+    assert (acc2 == full["acc2"][rows, cols]).all()
+    assert (y == full["y"][rows, cols]).all()
+    ref_acc = oracle_lib.dual_linear(d["x"], d["w_res"], d["l1t"], d["l2t"])["acc"]
+    assert (acc == ref_acc[rows, cols]).all()
+
+
 # ---------------------------------------------------------------- generators
 
 def test_generators_deterministic_and_outliers():
@@ -368,6 +381,8 @@ def test_generators_deterministic_and_outliers():
         assert a[k].tobytes() == b[k].tobytes()
     assert synth.outlier_count(0.005, 4096) == 20 and synth.outlier_count(0.01, 14336) == 143
     assert synth.outlier_count(0.001, 8192) == 8 and synth.outlier_count(4 / 512, 512) == 4
+    with pytest.raises(ValueError):
+        synth.make_random(4, 128, 16, 32, seed=0)  # rank above min(n, m)
     # the 4 outlier channels of the tiny config dominate the column maxima
     colmax = np.abs(a["x"].astype(np.float64)).max(axis=0)
     assert (np.sort(colmax)[-4:] > 10 * np.median(colmax)).all()

@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "TWQ_OK", 1: "TWQ_ERR_NULL", 2: "TWQ_ERR_SHAPE", 3: "TWQ_ERR_
 # every symbol include/twq.h declares
 EXPORTS = ("twq_status_string", "twq_last_error_string", "twq_version",
            "twq_quantize_act_workspace_bytes", "twq_quantize_act", "twq_pack_weight",
-           "twq_dual_linear", "twq_debug_residual_acc")
+           "twq_dual_linear", "twq_debug_residual_acc", "twq_pack_lowrank_int4",
+           "twq_lowrank_requant", "twq_dual_linear_lr4")
 
 
 class TwqError(RuntimeError):
@@ -69,6 +70,12 @@ def lib() -> ctypes.CDLL:
                 L.twq_dual_linear.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P]
                 L.twq_debug_residual_acc.restype = ctypes.c_int
                 L.twq_debug_residual_acc.argtypes = [_P, _P, _P, _I, _I, _I, _P]
+                L.twq_pack_lowrank_int4.restype = ctypes.c_int
+                L.twq_pack_lowrank_int4.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]
+                L.twq_lowrank_requant.restype = ctypes.c_int
+                L.twq_lowrank_requant.argtypes = [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _P]
+                L.twq_dual_linear_lr4.restype = ctypes.c_int
+                L.twq_dual_linear_lr4.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P]
                 _lib = L
     return _lib
 
@@ -190,6 +197,62 @@ def debug_residual_acc(qx, qw):
     _check(lib().twq_debug_residual_acc(_ptr(qx), _ptr(qw), _ptr(acc), b, 2 * kb, n,
                                         _stream(qx.device)), "twq_debug_residual_acc")
     return acc
+
+
+def pack_lowrank_int4(l1t: torch.Tensor, l2t: torch.Tensor):
+    """fp16 L1^T [r][m], L2^T [n][r] -> dict ql1 [r][m/2], sl1 [r], ql2 [n][r/2], sl2 [r], c [r]."""
+    _need(l1t, "l1t", torch.float16, 2)
+    _need(l2t, "l2t", torch.float16, 2)
+    r, m = l1t.shape
+    n = l2t.shape[0]
+    if l2t.shape[1] != r:
+        raise ValueError("l2t must be [n][r]")
+    dev = l1t.device
+    out = {"ql1": torch.empty((r, m // 2), dtype=torch.uint8, device=dev),
+           "sl1": torch.empty((r,), dtype=torch.float32, device=dev),
+           "ql2": torch.empty((n, r // 2), dtype=torch.uint8, device=dev),
+           "sl2": torch.empty((r,), dtype=torch.float32, device=dev),
+           "c": torch.empty((r,), dtype=torch.float32, device=dev)}
+    _check(lib().twq_pack_lowrank_int4(_ptr(l1t), _ptr(l2t), r, m, n, _ptr(out["ql1"]), _ptr(out["sl1"]),
+                                       _ptr(out["ql2"]), _ptr(out["sl2"]), _ptr(out["c"]), _stream(dev)),
+           "twq_pack_lowrank_int4")
+    return out
+
+
+def lowrank_requant(qx, sx, ql1, c):
+    """H = Q_X Q_L1^T (int32 [b][r]), Q_H u8 [b][r/2], s_H f32 [b]."""
+    _need(qx, "qx", torch.uint8, 2)
+    _need(sx, "sx", torch.float32, 1)
+    _need(ql1, "ql1", torch.uint8, 2)
+    _need(c, "c", torch.float32, 1)
+    b, kb = qx.shape
+    r = ql1.shape[0]
+    dev = qx.device
+    h = torch.empty((b, r), dtype=torch.int32, device=dev)
+    qh = torch.empty((b, r // 2), dtype=torch.uint8, device=dev)
+    sh = torch.empty((b,), dtype=torch.float32, device=dev)
+    _check(lib().twq_lowrank_requant(_ptr(qx), _ptr(sx), _ptr(ql1), _ptr(c), r, _ptr(h), _ptr(qh), _ptr(sh),
+                                     b, 2 * kb, _stream(dev)), "twq_lowrank_requant")
+    return h, qh, sh
+
+
+def dual_linear_lr4(qx, sx, qw, sw, qh, sh, ql2, out: torch.Tensor | None = None):
+    """The fused layer with the int4 low-rank branch: Y fp16 [b][n]."""
+    for name, t, dt in (("qx", qx, torch.uint8), ("qw", qw, torch.uint8), ("qh", qh, torch.uint8),
+                        ("ql2", ql2, torch.uint8)):
+        _need(t, name, dt, 2)
+    _need(sx, "sx", torch.float32, 1)
+    _need(sw, "sw", torch.float32, 1)
+    _need(sh, "sh", torch.float32, 1)
+    b, kb = qx.shape
+    n = qw.shape[0]
+    r = 2 * qh.shape[1]
+    if ql2.shape != (n, r // 2) or sh.shape[0] != b:
+        raise ValueError("qh must be [b][r/2], ql2 [n][r/2], sh [b]")
+    y = out if out is not None else torch.empty((b, n), dtype=torch.float16, device=qx.device)
+    _check(lib().twq_dual_linear_lr4(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(qh), _ptr(sh), _ptr(ql2), r,
+                                     _ptr(y), b, 2 * kb, n, _stream(qx.device)), "twq_dual_linear_lr4")
+    return y
 
 
 class DualLinear:

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "lib", "libtwq.so")
-SOURCES = ["act_quant.hip", "pack_weight.hip", "dual_linear.hip", "twq_api.cpp"]
+SOURCES = ["act_quant.hip", "pack_weight.hip", "dual_linear.hip", "lowrank_int4.hip", "twq_api.cpp"]
 ARCH = "gfx950"
 
 

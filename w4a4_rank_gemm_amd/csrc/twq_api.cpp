@@ -29,6 +29,7 @@ bool valid_m(int64_t m) { return m > 0 && m % 128 == 0 && m <= kMaxM; }
 bool valid_b(int64_t b) { return b >= 0 && b <= kMaxTokens; }
 bool valid_n(int64_t n) { return n >= 0 && n % 16 == 0 && n <= kMaxN; }
 bool valid_r(int64_t r) { return r >= 0 && r % 16 == 0 && r <= kMaxRank; }
+bool valid_r4(int64_t r) { return r >= 0 && r % 32 == 0 && r <= kMaxRank; }  // int4 low-rank variant
 
 }  // namespace
 
@@ -133,6 +134,61 @@ twq_status twq_debug_residual_acc(const void *qx, const void *qw, int32_t *acc, 
     a.n = n;
     const hipError_t e = twq::launch_dual_linear(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_debug_residual_acc");
+}
+
+twq_status twq_pack_lowrank_int4(const void *l1t, const void *l2t, int64_t r, int64_t m, int64_t n, void *ql1,
+                                 float *sl1, void *ql2, float *sl2, float *c, void *stream) {
+    if (!valid_r4(r) || !valid_m(m) || !valid_n(n)) return TWQ_ERR_SHAPE;
+    if (r == 0) return TWQ_OK;
+    if (!l1t || !l2t || !ql1 || !sl1 || !ql2 || !sl2 || !c) return TWQ_ERR_NULL;
+    if (!aligned16(l1t) || !aligned16(l2t) || !aligned16(ql1) || !aligned16(sl1) || !aligned16(ql2) ||
+        !aligned16(sl2) || !aligned16(c))
+        return TWQ_ERR_ALIGN;
+    const hipError_t e = twq::launch_pack_lowrank(static_cast<const uint16_t *>(l1t), static_cast<const uint16_t *>(l2t),
+                                                  (int)r, m, n, static_cast<uint8_t *>(ql1), sl1,
+                                                  static_cast<uint8_t *>(ql2), sl2, c, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_pack_lowrank_int4");
+}
+
+twq_status twq_lowrank_requant(const void *qx, const float *sx, const void *ql1, const float *c, int64_t r, int32_t *h,
+                               void *qh, float *sh, int64_t b, int64_t m, void *stream) {
+    if (!valid_b(b) || !valid_m(m) || !valid_r4(r)) return TWQ_ERR_SHAPE;
+    if (b == 0 || r == 0) return TWQ_OK;
+    if (!qx || !sx || !ql1 || !c || !h || !qh || !sh) return TWQ_ERR_NULL;
+    if (!aligned16(qx) || !aligned16(sx) || !aligned16(ql1) || !aligned16(c) || !aligned16(h) || !aligned16(qh) ||
+        !aligned16(sh))
+        return TWQ_ERR_ALIGN;
+    const hipError_t e = twq::launch_lowrank_requant(
+        static_cast<const uint8_t *>(qx), sx, static_cast<const uint8_t *>(ql1), c, (int)r, h,
+        static_cast<uint8_t *>(qh), sh, b, m, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_lowrank_requant");
+}
+
+twq_status twq_dual_linear_lr4(const void *qx, const float *sx, const void *qw, const float *sw, const void *qh,
+                               const float *sh, const void *ql2, int64_t r, void *y, int64_t b, int64_t m, int64_t n,
+                               void *stream) {
+    if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r4(r)) return TWQ_ERR_SHAPE;
+    if (b == 0 || n == 0) return TWQ_OK;
+    if (!qx || !sx || !qw || !sw || !y) return TWQ_ERR_NULL;
+    if (r > 0 && (!qh || !sh || !ql2)) return TWQ_ERR_NULL;
+    if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(sw) || !aligned16(y)) return TWQ_ERR_ALIGN;
+    if (r > 0 && (!aligned16(qh) || !aligned16(sh) || !aligned16(ql2))) return TWQ_ERR_ALIGN;
+    twq::DualArgs a{};
+    a.qx = static_cast<const uint8_t *>(qx);
+    a.sx = sx;
+    a.qw = static_cast<const uint8_t *>(qw);
+    a.sw = sw;
+    a.r = (int)r;
+    a.y = static_cast<uint16_t *>(y);
+    a.b = b;
+    a.m = m;
+    a.n = n;
+    a.lr4 = 1;
+    a.qh = static_cast<const uint8_t *>(qh);
+    a.sh = sh;
+    a.ql2 = static_cast<const uint8_t *>(ql2);
+    const hipError_t e = twq::launch_dual_linear(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_dual_linear_lr4");
 }
 
 }  // extern "C"

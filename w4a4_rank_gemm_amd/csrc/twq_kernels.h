@@ -54,10 +54,21 @@ struct DualArgs {
     const uint16_t *l2t;
     int r;
     uint16_t *y;       // fp16 [b][n]
-    int32_t *acc;      // debug: int32 [b][n] instead of y
+    int32_t *acc;      // int32 [b][n] instead of y (the exact integer sum)
     int64_t b, m, n;
+    int lr4;           // int4 low-rank branch: y += s_H (Q_H Q_L2^T) instead of T L2
+    const uint8_t *qh; // [b][r/2] packed Q_H
+    const float *sh;   // [b]
+    const uint8_t *ql2;// [n][r/2] packed Q_L2
 };
 
 hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream);
+
+// ---- int4 low-rank variant ------------------------------------------------------------
+
+hipError_t launch_pack_lowrank(const uint16_t *l1t, const uint16_t *l2t, int r, int64_t m, int64_t n, uint8_t *ql1,
+                               float *sl1, uint8_t *ql2, float *sl2, float *c, hipStream_t stream);
+hipError_t launch_lowrank_requant(const uint8_t *qx, const float *sx, const uint8_t *ql1, const float *c, int r,
+                                  int32_t *h, uint8_t *qh, float *sh, int64_t b, int64_t m, hipStream_t stream);
 
 }  // namespace twq
