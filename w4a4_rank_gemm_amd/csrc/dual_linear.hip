@@ -19,6 +19,8 @@
 // accumulator set. The i32 and f32 16x16 results share one register layout. In
 // the int4 low-rank variant the epilogue instead adds s_H (Q_H Q_L2^T), a second
 // int8 matrix product over the rank dimension.
+#include <utility>
+
 #include "twq_device.h"
 #include "twq_kernels.h"
 
@@ -225,9 +227,17 @@ static hipError_t launch_decode(const DualArgs &a, hipStream_t stream) {
 // tile of Y^T (BN output channels by BM tokens) and streams K in stages of 128 codes
 // (64 bytes per row) through a ring of S stages in LDS, filled by direct global ->
 // LDS loads (global_load_lds_dwordx4: no register staging, S - 1 stages in flight).
-// Each lane's 16 bytes land at the next 16-byte slot of its wave's LDS window, so
-// the XOR swizzle of the 16-byte chunks is applied by choosing which chunk each lane
-// fetches. Waves read their operands back, expand them to int8 (unpack16) and issue
+// A stage holds the 128-code K slice of the tile's BN weight rows and BM token rows
+// (64 bytes per row) as 1 KB blocks of 16 rows. Inside a block, rows 2s and 2s + 1
+// share the 128-byte line s (s = 0..7): the 16-byte chunk c of row 2s + h has logical
+// position 4h + c in the line and is stored at position (4h + c) ^ s. Both sides of the
+// stage run at full rate with this layout on gfx950 (measured):
+//  - the direct-to-LDS loads write a wave's 64 lanes to 64 consecutive 16-byte slots,
+//    and with this layout every 4-lane quad fetches one row's contiguous 64 bytes
+//    (only the order inside the quad is permuted), which the memory pipeline coalesces;
+//  - an MFMA operand wants row li, chunk g in lane li + 16 g; those reads hit every
+//    bank group evenly (plain 64-byte rows, swizzled or not, run at half rate).
+// Waves read their operands back, expand them to int8 (unpack16) and issue
 // v_mfma_i32_16x16x64_i8. Rows past n or b are clamped to a valid row (their outputs
 // are never stored); m is a multiple of 128, so stages never run past a row.
 // Block indices are mapped to tiles XCD by XCD (the hardware deals consecutive CTAs
@@ -236,10 +246,7 @@ static hipError_t launch_decode(const DualArgs &a, hipStream_t stream) {
 // that XCD's L2.
 constexpr int kStageRowBytes = 64;
 
-// chunk swizzle for 64-byte LDS rows; conflict-free for 8 lanes (32 banks) or 16
-// lanes (64 banks) reading the same logical chunk of consecutive rows
-__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-
+constexpr int kBlockBytes = 1024;  // 16 rows x 64 bytes
 // Block b runs on XCD b % 8 (the hardware deals CTAs out in turn). Give XCD x the
 // contiguous range of q + (x < rem) tiles starting at x q + min(x, rem), q = tiles / 8,
 // rem = tiles % 8: a bijection of [0, tiles) for any tile count.
@@ -255,6 +262,49 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// LDS byte offset of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// The eight operand reads of one stage: four consecutive 1 KB blocks from address a
+// and four from address b (each plus OFF), completed before returning (the wait is
+// part of the same asm statement, so no output register is live while its load is in
+// flight). Written as one statement because the compiler cannot tell these reads
+// apart from the direct-to-LDS loads still in flight into other ring slots, and would
+// otherwise wait for all of those first. The offsets ride in the instructions'
+// 16-bit immediate field.
+template <int OFF>
+__device__ __forceinline__ void lds_read_4x4(uint32_t a, uint32_t b, v4i (&r)[8]) {
+    static_assert(OFF >= 0 && OFF + 3 * kBlockBytes < 65536, "ds_read immediate offset");
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%10\n\t"
+        "ds_read_b128 %1, %8 offset:%11\n\t"
+        "ds_read_b128 %2, %8 offset:%12\n\t"
+        "ds_read_b128 %3, %8 offset:%13\n\t"
+        "ds_read_b128 %4, %9 offset:%10\n\t"
+        "ds_read_b128 %5, %9 offset:%11\n\t"
+        "ds_read_b128 %6, %9 offset:%12\n\t"
+        "ds_read_b128 %7, %9 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7])
+        : "v"(a), "v"(b), "n"(OFF), "n"(OFF + kBlockBytes), "n"(OFF + 2 * kBlockBytes), "n"(OFF + 3 * kBlockBytes)
+        : "memory");
+}
+
+// Workgroup barrier without the memory fence __syncthreads adds (which waits for every
+// outstanding load); callers first wait for their own loads of the stage they need.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int... I, class F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &&f) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
 template <int BN, int BM, int WN, int WM, int S, int GM, bool STORE_ACC>
 __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     constexpr int NT = WN * WM * 64;
@@ -264,7 +314,6 @@ __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int t
     constexpr int DPT = ROWS * 4 / NT;  // 16-byte DMA loads per thread per stage
     static_assert(ROWS * 4 % NT == 0 && FN >= 1 && FM >= 1, "tile shape");
     static_assert((S - 2) * DPT < 64, "outstanding loads fit vmcnt");
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int li = lane & 15, g = lane >> 4;
@@ -281,29 +330,38 @@ __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int t
     const int64_t kb = a.m / 2;
     const int nst = (int)(a.m / 128);
 
-    // this thread's DMA sources: slot q = j * NT + tid of each stage
-    const uint8_t *src[DPT];
+    // this thread's DMA sources: slot q = j * NT + tid of each stage is position
+    // q % 8 of line (q % 64) / 8 of block q / 64. Each j lies wholly in the weight rows
+    // or wholly in the token rows, so its address is a uniform tile base (advanced by
+    // 64 bytes per stage) plus a 32-bit per-lane offset.
+    static_assert(NT % 64 == 0 && (BN * 4) % NT == 0, "each DMA group in one operand");
+    const uint8_t *wbase = a.qw + ch0 * kb, *xbase = a.qx + tok0 * kb;
+    uint32_t off[DPT];
 #pragma unroll
     for (int j = 0; j < DPT; ++j) {
         const int q = j * NT + tid;
-        const int row = q / 4, phys = q % 4;
-        const int logical = phys ^ swz4(row);
-        const uint8_t *base;
+        const int line = (q % 64) / 8, logical = (q % 8) ^ line;
+        const int row = (q / 64) * 16 + 2 * line + logical / 4, chunk = logical % 4;
+        int64_t rel;  // row offset from the tile's first row, clamped into the operand
         if (row < BN) {
             const int64_t ch = ch0 + row;
-            base = a.qw + (ch < a.n ? ch : a.n - 1) * kb;
+            rel = (ch < a.n ? ch : a.n - 1) - ch0;
         } else {
             const int64_t tok = tok0 + row - BN;
-            base = a.qx + (tok < a.b ? tok : a.b - 1) * kb;
+            rel = (tok < a.b ? tok : a.b - 1) - tok0;
         }
-        src[j] = base + logical * 16;
+        off[j] = (uint32_t)(rel * kb + chunk * 16);
     }
-    auto issue = [&](int st) {
-        uint8_t *dst = lds + (st % S) * STAGE_BYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[S * STAGE_BYTES];
+    auto issue = [&](int st, auto slot) {
+        uint8_t *dst = ring + decltype(slot)::value * STAGE_BYTES;
+        const uint8_t *wst = wbase + (int64_t)st * kStageRowBytes, *xst = xbase + (int64_t)st * kStageRowBytes;
 #pragma unroll
-        for (int j = 0; j < DPT; ++j)
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src[j] + (int64_t)st * kStageRowBytes),
+        for (int j = 0; j < DPT; ++j) {
+            const uint8_t *src = ((j * NT) / 4 < BN ? wst : xst) + off[j];
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
                                              reinterpret_cast<void *>(dst + (j * NT + wave * kWave) * 16), 16, 0, 0);
+        }
     };
 
     v4i acc[FN][FM];
@@ -312,37 +370,43 @@ __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int t
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = v4i{0, 0, 0, 0};
 
-#pragma unroll
-    for (int st = 0; st < S - 1; ++st)
-        if (st < nst) issue(st);
-    for (int st = 0; st < nst; ++st) {
-        if (st + S - 2 < nst)
-            wait_vmcnt<(S - 2) * DPT>();
-        else
-            wait_vmcnt<0>();
-        __syncthreads();  // stage st landed for every thread; stage st - 1 consumed by every wave
-        if (st + S - 1 < nst) issue(st + S - 1);
-        const uint8_t *L = lds + (st % S) * STAGE_BYTES;
-        v4i alo[FN], ahi[FN], blo[FM], bhi[FM];
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int row = wn * (BN / WN) + fn * 16 + li;
-            unpack16(*reinterpret_cast<const uint4 *>(L + row * kStageRowBytes + ((g ^ swz4(row)) * 16)), alo[fn],
-                     ahi[fn]);
-        }
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int row = BN + wm * (BM / WM) + fm * 16 + li;
-            unpack16(*reinterpret_cast<const uint4 *>(L + row * kStageRowBytes + ((g ^ swz4(row)) * 16)), blo[fm],
-                     bhi[fm]);
-        }
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                acc[fn][fm] = mfma_i8(alo[fn], blo[fm], acc[fn][fm]);
-                acc[fn][fm] = mfma_i8(ahi[fn], bhi[fm], acc[fn][fm]);
+    // this lane's operand addresses: FN weight blocks from rda, FM token blocks from rdb
+    static_assert(FN == 4 && FM == 4, "the stage reader loads four weight and four token blocks per wave");
+    // row li, chunk g of a block: line li / 2, logical position 4 (li % 2) + g
+    const uint32_t ring0 = lds_offset(ring) + (li / 2) * 128 + ((4 * (li % 2) + g) ^ (li / 2)) * 16;
+    const uint32_t rda = ring0 + (wn * (BN / WN) / 16) * kBlockBytes;
+    const uint32_t rdb = ring0 + ((BN + wm * (BM / WM)) / 16) * kBlockBytes;
+
+    // Step st issues stage st into slot st % S and consumes stage st - (S - 1). Every
+    // step issues (past the last stage it loads the last stage again, into a slot no
+    // later step reads), so the count of loads in flight is the same at every wait and
+    // the compiler sees no branch around a load. The loop is unrolled by the ring
+    // depth, so every slot is a compile-time constant.
+    for (int s0 = 0; s0 < nst + S - 1; s0 += S) {
+        static_for(std::make_integer_sequence<int, S>{}, [&](auto u) {
+            const int st = s0 + u, c = st - (S - 1);
+            if (c >= nst) return;
+            if (c >= 0) {
+                wait_vmcnt<(S - 2) * DPT>();
+                stage_barrier();  // stage c landed for every thread; stage c - 1 consumed by every wave
             }
+            issue(st < nst ? st : nst - 1, u);
+            if (c < 0) return;
+            v4i raw[8];
+            lds_read_4x4<((u + 1) % S) * STAGE_BYTES>(rda, rdb, raw);  // slot of stage c = st - (S - 1)
+            v4i alo[FN], ahi[FN], blo[FM], bhi[FM];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) unpack16(raw[fn], alo[fn], ahi[fn]);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) unpack16(raw[FN + fm], blo[fm], bhi[fm]);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    acc[fn][fm] = mfma_i8(alo[fn], blo[fm], acc[fn][fm]);
+                    acc[fn][fm] = mfma_i8(ahi[fn], bhi[fm], acc[fn][fm]);
+                }
+        });
     }
 
     // lane (li, g), register v of tile (fn, fm) holds channel ch_base + 4g + v, token tok_base + li
@@ -431,16 +495,10 @@ template <int BN, int BM, int WN, int WM, int S, int GM>
 static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
     const int64_t tiles_n = (a.n + BN - 1) / BN, tiles_m = (a.b + BM - 1) / BM;
     const dim3 grid((unsigned)(tiles_n * tiles_m)), block(WN * WM * 64);
-    const size_t lds = (size_t)S * (BN + BM) * kStageRowBytes;
-    if (a.acc) {
-        auto k = dual_linear_pf<BN, BM, WN, WM, S, GM, true>;
-        hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL(k, grid, block, lds, stream, a, (int)tiles_n, (int)tiles_m);
-    } else {
-        auto k = dual_linear_pf<BN, BM, WN, WM, S, GM, false>;
-        hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL(k, grid, block, lds, stream, a, (int)tiles_n, (int)tiles_m);
-    }
+    if (a.acc)
+        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, true>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
+    else
+        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, false>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
     return hipGetLastError();
 }
 

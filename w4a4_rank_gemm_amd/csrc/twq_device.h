@@ -73,6 +73,10 @@ __device__ __forceinline__ void unpack16(const uint4 raw, v4i &lo, v4i &hi) {
     hi[3] = (int)((raw.w << 4) & M);
 }
 
+__device__ __forceinline__ void unpack16(const v4i raw, v4i &lo, v4i &hi) {
+    unpack16(make_uint4((uint32_t)raw[0], (uint32_t)raw[1], (uint32_t)raw[2], (uint32_t)raw[3]), lo, hi);
+}
+
 __device__ __forceinline__ v4i mfma_i8(const v4i a, const v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
