@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="o_proj_decode")
+    ap.add_argument("--path", choices=("linear", "split"), default="linear",
+                    help="linear: one twq_linear call per step; split: twq_quantize_act + twq_dual_linear")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate over (0: auto)")
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
@@ -159,8 +161,13 @@ def main():
             "y": torch.empty((b, n), dtype=torch.float16, device=dev),
         })
     L = twq.lib()
-    ws, wsb = twq._workspace(dev, L.twq_quantize_act_workspace_bytes(b, m, r))
+    ws, wsb = twq._workspace(dev, max(L.twq_quantize_act_workspace_bytes(b, m, r),
+                                      L.twq_linear_workspace_bytes(b, m, n, r)))
     P = lambda t: None if t is None else twq.ctypes.c_void_p(t.data_ptr())
+
+    def layer(s, stream):
+        twq._check(L.twq_linear(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["l1t"]), P(s["l2t"]), r, P(s["y"]),
+                                b, m, n, P(ws), wsb, stream), "twq_linear")
 
     def quant(s, stream):
         twq._check(L.twq_quantize_act(P(s["x"]), b, m, P(s["qx"]), P(s["sx"]), P(s["l1t"]), r, P(s["t"]),
@@ -184,13 +191,19 @@ def main():
         return twq.ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
     def steps_fn(k, with_quant=True, offset=0):
+        # with_quant=False: the main-loop kernel alone (twq_dual_linear on the Q_X,
+        # s_X and T of an earlier call), for its launch duration
         def run():
             st = hs()
             for i in range(k):
                 s = sets[(i + offset) % copies]
-                if with_quant:
+                if not with_quant:
+                    dual(s, st)
+                elif args.path == "linear":
+                    layer(s, st)
+                else:
                     quant(s, st)
-                dual(s, st)
+                    dual(s, st)
         return run
 
     def timed(fn_or_graph, is_graph):
@@ -207,8 +220,11 @@ def main():
         return e0.elapsed_time(e1)  # ms
 
     with torch.cuda.stream(stream):
-        # one eager call first (lazy initialisation, workspace), then the warmup steps
+        # one eager call first (lazy initialisation, workspace), then the warmup steps;
+        # Q_X, s_X and T of every copy are filled once for the kernel-only timing
         steps_fn(1)()
+        for s_ in sets:
+            quant(s_, hs())
         torch.cuda.synchronize()
         if args.eager:
             steps_fn(args.warmup)()
@@ -265,6 +281,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.config}: b={b} m={m} n={n} r={r}", "b": b, "m": m, "n": n, "r": r,
                    "weight_copies_rotated": copies, "launch": "eager" if args.eager else "hip_graph",
+                   "entry_points": "twq_linear" if args.path == "linear" else "twq_quantize_act+twq_dual_linear",
                    "call_bytes": call_bytes(b, m, n, r),
                    "hbm_frac_whole_call": round(call_bytes(b, m, n, r) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                    "int8_mfma_frac_whole_call": round(2 * b * m * n / (ms_step * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)},

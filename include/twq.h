@@ -131,6 +131,27 @@ twq_status twq_debug_residual_acc(const void *qx, const void *qw, int32_t *acc, 
                                   int64_t m, int64_t n, void *stream);
 
 /*
+ * The whole layer in one call: the activation quantizer and T = X L1 (as for
+ * twq_quantize_act), then the fused layer (as for twq_dual_linear), with Q_X, s_X
+ * and T kept in the workspace. TwinQuant page 1, section 4.3 describes the layer as
+ * one fused step; here the first low-rank product and the quantizer still run
+ * first, but with few tokens T is never reduced to one array: its partial sums
+ * over K slices go straight to the epilogue of the main loop, which adds them in
+ * slice order (the same order and values twq_quantize_act would give T), saving a
+ * launch. Y is bitwise the result of twq_quantize_act + twq_dual_linear.
+ *
+ *   x     fp16 [b][m];  qw, sw from twq_pack_weight;  l1t, l2t as above (NULL iff r == 0)
+ *   y     fp16 [b][n]     (out)
+ *   workspace, workspace_bytes         at least twq_linear_workspace_bytes(b, m, n, r)
+ *                                      bytes; no initial contents are needed. Calls
+ *                                      that share a workspace must not overlap in time.
+ */
+size_t twq_linear_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r);
+twq_status twq_linear(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t,
+                      int64_t r, void *y, int64_t b, int64_t m, int64_t n, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
  * ---- int4 low-rank variant (TwinQuant page 1, section 4.3) ----
  *
  * Both low-rank factors in 4 bits: the first low-rank GEMM gives INT32 H = Q_X Q_L1,

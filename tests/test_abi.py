@@ -111,3 +111,17 @@ def test_lowrank_int4_validation():
     assert L.twq_pack_lowrank_int4(None, None, 0, 256, 32, None, None, None, None, None, None) == OK
     assert L.twq_lowrank_requant(None, None, None, None, 32, None, None, None, 0, 256, None) == OK
     assert L.twq_dual_linear_lr4(None, None, None, None, None, None, None, 32, None, 0, 256, 32, None) == OK
+
+
+def test_linear_validation():
+    L = twq.lib()
+    need = L.twq_linear_workspace_bytes(16, 4096, 4096, 32)
+    assert need >= 16 * 4096 // 2 + 16 * 4
+    assert L.twq_linear_workspace_bytes(16, 100, 4096, 32) == 0
+    assert L.twq_linear(A, A, A, A, A, 32, A, 16, 4096, 4096, A, need - 1, None) == WORKSPACE
+    assert L.twq_linear(A, A, A, A, A, 32, A, 16, 4096, 4096, None, need, None) == WORKSPACE
+    assert L.twq_linear(A, A, A, None, A, 32, A, 16, 4096, 4096, A, need, None) == NULL
+    assert L.twq_linear(MIS, A, A, A, A, 32, A, 16, 4096, 4096, A, need, None) == ALIGN
+    assert L.twq_linear(A, A, A, A, A, 24, A, 16, 4096, 4096, A, need, None) == SHAPE
+    assert L.twq_linear(A, A, A, A, A, 32, A, 16, 4096, 40, A, need, None) == SHAPE
+    assert L.twq_linear(None, None, None, None, None, 32, None, 0, 4096, 4096, None, 0, None) == OK

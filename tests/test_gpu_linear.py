@@ -1,0 +1,76 @@
+"""The one-call layer (twq_linear) against the oracle and against the separate calls.
+
+twq_linear adds the partial sums of T in the epilogue for few tokens (in slice order,
+as twq_quantize_act does), so its Y equals twq_quantize_act + twq_dual_linear value for
+value; both are checked against the oracle to 2e-3 * max|Y_oracle|.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w4a4_rank_gemm_amd as twq
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 2e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(d):
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(d["x"]).to(dev)
+    qw, sw = twq.pack_weight(torch.from_numpy(d["w_res"]).to(dev))
+    r = d["l1t"].shape[0]
+    l1t = torch.from_numpy(d["l1t"]).to(dev) if r else None
+    l2t = torch.from_numpy(d["l2t"]).to(dev) if r else None
+    y1 = twq.linear(x, qw, sw, l1t, l2t)
+    qx, sx, t = twq.quantize_act(x, l1t)
+    y2 = twq.dual_linear(qx, sx, qw, sw, t, l2t)
+    torch.cuda.synchronize()
+    return y1.cpu().numpy(), y2.cpu().numpy()
+
+
+# few tokens (partial sums of T added in the epilogue, 2 to 16 slices, one or two
+# channel tiles per CTA), the decode shapes that need T whole, and many tokens
+SHAPES = [(16, 4096, 4096, 32), (16, 512, 512, 16), (1, 4096, 272, 32), (5, 2048, 16384, 64),
+          (16, 8192, 1024, 128), (24, 4096, 4096, 32), (32, 1024, 8192, 64), (48, 2048, 512, 16),
+          (64, 4096, 2048, 32), (200, 1024, 528, 48), (16, 4096, 4096, 0), (3, 16384, 256, 256)]
+
+
+@pytest.mark.parametrize("b,m,n,r", SHAPES)
+def test_linear_matches_split_calls_and_oracle(b, m, n, r):
+    _say(f"twq_linear b={b} m={m} n={n} r={r}")
+    d = synth.make_random(b, m, n, r, seed=11 * b + r)
+    y1, y2 = _run(d)
+    assert np.array_equal(y1, y2), "twq_linear differs from twq_quantize_act + twq_dual_linear"
+    ref = oracle.dual_linear(d["x"], d["w_res"], d["l1t"], d["l2t"])["y"]
+    err = np.abs(y1.astype(np.float64) - ref).max()
+    assert err <= Y_TOL * np.abs(ref).max(), (err, np.abs(ref).max())
+
+
+def test_linear_headline_config_full():
+    """The o_proj decode layer (b=16, m=n=4096, r=32), every output against the oracle."""
+    d = synth.make_layer("o_proj_decode")
+    y1, y2 = _run(d)
+    assert np.array_equal(y1, y2)
+    ref = oracle.dual_linear(d["x"], d["w_res"], d["l1t"], d["l2t"])["y"]
+    err = np.abs(y1.astype(np.float64) - ref).max()
+    assert err <= Y_TOL * np.abs(ref).max(), (err, np.abs(ref).max())
+
+
+def test_linear_repeat_bitwise():
+    d = synth.make_random(16, 4096, 1024, 32, seed=5)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(d["x"]).to(dev)
+    qw, sw = twq.pack_weight(torch.from_numpy(d["w_res"]).to(dev))
+    l1t, l2t = torch.from_numpy(d["l1t"]).to(dev), torch.from_numpy(d["l2t"]).to(dev)
+    ys = [twq.linear(x, qw, sw, l1t, l2t).cpu() for _ in range(3)]
+    assert all(torch.equal(ys[0], y) for y in ys[1:])

@@ -27,8 +27,8 @@ STATUS_NAMES = {0: "TWQ_OK", 1: "TWQ_ERR_NULL", 2: "TWQ_ERR_SHAPE", 3: "TWQ_ERR_
 # every symbol include/twq.h declares
 EXPORTS = ("twq_status_string", "twq_last_error_string", "twq_version",
            "twq_quantize_act_workspace_bytes", "twq_quantize_act", "twq_pack_weight",
-           "twq_dual_linear", "twq_debug_residual_acc", "twq_pack_lowrank_int4",
-           "twq_lowrank_requant", "twq_dual_linear_lr4")
+           "twq_dual_linear", "twq_debug_residual_acc", "twq_linear_workspace_bytes",
+           "twq_linear", "twq_pack_lowrank_int4", "twq_lowrank_requant", "twq_dual_linear_lr4")
 
 
 class TwqError(RuntimeError):
@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
                 L.twq_dual_linear.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P]
                 L.twq_debug_residual_acc.restype = ctypes.c_int
                 L.twq_debug_residual_acc.argtypes = [_P, _P, _P, _I, _I, _I, _P]
+                L.twq_linear_workspace_bytes.restype = _S
+                L.twq_linear_workspace_bytes.argtypes = [_I, _I, _I, _I]
+                L.twq_linear.restype = ctypes.c_int
+                L.twq_linear.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _S, _P]
                 L.twq_pack_lowrank_int4.restype = ctypes.c_int
                 L.twq_pack_lowrank_int4.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]
                 L.twq_lowrank_requant.restype = ctypes.c_int
@@ -187,6 +191,38 @@ def dual_linear(qx, sx, qw, sw, t=None, l2t=None, out: torch.Tensor | None = Non
     return y
 
 
+def linear(x: torch.Tensor, qw, sw, l1t=None, l2t=None, out: torch.Tensor | None = None):
+    """The whole layer in one call (twq_linear): Y fp16 [b][n] from fp16 X, the packed
+    residual weight and the fp16 low-rank pair; Q_X, s_X and T live in the workspace."""
+    _need(x, "x", torch.float16, 2)
+    _need(qw, "qw", torch.uint8, 2)
+    _need(sw, "sw", torch.float32, 1)
+    b, m = x.shape
+    n = qw.shape[0]
+    if qw.shape[1] != m // 2 or sw.shape[0] != n:
+        raise ValueError("inconsistent shapes of x/qw/sw")
+    r = 0
+    if l1t is not None or l2t is not None:
+        _need(l1t, "l1t", torch.float16, 2)
+        _need(l2t, "l2t", torch.float16, 2)
+        r = l1t.shape[0]
+        if l1t.shape[1] != m or l2t.shape != (n, r):
+            raise ValueError("l1t must be [r][m] and l2t [n][r]")
+    dev = x.device
+    for name, ten in (("qw", qw), ("sw", sw), ("l1t", l1t), ("l2t", l2t)):
+        if ten is not None and ten.device != dev:
+            raise ValueError(f"{name} is on {ten.device}, x on {dev}")
+    y = out if out is not None else torch.empty((b, n), dtype=torch.float16, device=dev)
+    _need(y, "out", torch.float16, 2)
+    if y.shape != (b, n):
+        raise ValueError("out must be [b][n]")
+    L = lib()
+    ws, wsb = _workspace(dev, L.twq_linear_workspace_bytes(b, m, n, r))
+    _check(L.twq_linear(_ptr(x), _ptr(qw), _ptr(sw), _ptr(l1t), _ptr(l2t), r, _ptr(y), b, m, n,
+                        _ptr(ws), wsb, _stream(dev)), "twq_linear")
+    return y
+
+
 def debug_residual_acc(qx, qw):
     """int32 [b][n] = Q_X . Q_W^T computed by the fused kernel's main loop."""
     _need(qx, "qx", torch.uint8, 2)
@@ -266,5 +302,4 @@ class DualLinear:
         self.r = 0 if l1t is None else l1t.shape[0]
 
     def __call__(self, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-        qx, sx, t = quantize_act(x, self.l1t if self.r else None)
-        return dual_linear(qx, sx, self.qw, self.sw, t, self.l2t if self.r else None, out=out)
+        return linear(x, self.qw, self.sw, self.l1t if self.r else None, self.l2t if self.r else None, out=out)

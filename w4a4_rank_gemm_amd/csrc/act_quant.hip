@@ -341,7 +341,7 @@ hipError_t launch_act(const ActArgs &a, const ActPlan &pl, hipStream_t stream) {
                                  : launch_nt<1>(a.r > 0 ? pl.fm : 1, a, p, grid, stream);
     if (!ok) return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.r == 0 || pl.ks == 1) return e;
+    if (e != hipSuccess || a.r == 0 || pl.ks == 1 || a.keep_partials) return e;
     const int64_t n4 = a.b * a.r / 4;
     const int64_t rows_pad = pl.mode == 0 ? (int64_t)pl.row_tiles * 64 : (int64_t)pl.fm * 16;
     hipLaunchKernelGGL(t_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a.partials, a.b,

@@ -57,7 +57,10 @@ __device__ __forceinline__ v4i lr4_tile(const DualArgs &a, int64_t ch_row, int64
 // valid row and their outputs never stored -- so nothing serialises them, and the
 // low-rank operands of the epilogue are loaded first so their latency hides under
 // the main loop.
-template <int FN, int FM, int U, int RS, bool STORE_ACC, int NW = 4>
+// T partial-sum slices the decode epilogue adds itself, per 32-rank step it loads
+constexpr int kMaxTSlices = 16;
+
+template <int FN, int FM, int U, int RS, bool STORE_ACC, int TK = 1, int NW = 4>
 __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
     __shared__ v4i red[NW][FN * FM][kWave];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -82,24 +85,33 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
 
     // Epilogue tiles are dealt to the waves in turn (tile t to wave t % NW). When a
     // wave owns one tile, its low-rank operands are loaded here, ahead of the main
-    // loop (rank steps past r are loaded from rank 0 and zeroed where used).
+    // loop (rank steps past r are loaded from rank 0 and zeroed where used). T may come
+    // as up to TK partial sums over K slices; they are all loaded here and added in
+    // slice order in the epilogue.
     constexpr int TILES = FN * FM;
     constexpr bool PREFETCH = !STORE_ACC && RS > 0 && TILES <= NW;  // fp16 low-rank branch only
+    constexpr int TKS = PREFETCH ? TK : 1;
+    static_assert(TK == 1 || TK * RS <= kMaxTSlices, "partial sums of T held per lane");
     v8h l2f[PREFETCH ? RS : 1];
-    float4 tf[PREFETCH ? RS : 1][2];
-    if (PREFETCH && !a.lr4) {
-        const int t0 = wave < TILES ? wave : 0;
+    float4 tf[PREFETCH ? RS : 1][TKS][2];
+    if (PREFETCH && !a.lr4 && wave < TILES) {
+        const int t0 = wave;
         const int64_t chr = ch0 + (t0 / FM) * 16 + li, tokr = (t0 % FM) * 16 + li;
         const uint16_t *l2row = a.l2t + (chr < a.n ? chr : a.n - 1) * a.r;
-        const float *trow = a.t + (tokr < a.b ? tokr : a.b - 1) * a.r;
+        const float *trow = a.tpart + (tokr < a.b ? tokr : a.b - 1) * a.r;
 #pragma unroll
         for (int s = 0; s < RS; ++s) {
             const int rank = s * 32 + g * 8;
             const int rk = rank < a.r ? rank : 0;
             l2f[s] = load_h8(l2row + rk);
-            tf[s][0] = *reinterpret_cast<const float4 *>(trow + rk);
-            tf[s][1] = *reinterpret_cast<const float4 *>(trow + rk + 4);
+#pragma unroll
+            for (int k = 0; k < TKS; ++k) {  // unconditional (slices past tks reload slice 0), so none is sunk to its use
+                const int64_t kk = k < a.tks ? k : 0;
+                tf[s][k][0] = *reinterpret_cast<const float4 *>(trow + kk * a.tstride + rk);
+                tf[s][k][1] = *reinterpret_cast<const float4 *>(trow + kk * a.tstride + rk + 4);
+            }
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     v4i acc[FN][FM];
@@ -178,7 +190,14 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
 #pragma unroll
                 for (int s = 0; s < RS; ++s) {
                     const bool live = s * 32 + g * 8 < a.r;
-                    y = mfma_f16(l2f[s], live ? f32x8_to_h8(tf[s][0], tf[s][1]) : v8h{}, y);
+                    float4 t0 = tf[s][0][0], t1 = tf[s][0][1];
+#pragma unroll
+                    for (int k = 1; k < TKS; ++k)
+                        if (k < a.tks) {
+                            t0.x += tf[s][k][0].x; t0.y += tf[s][k][0].y; t0.z += tf[s][k][0].z; t0.w += tf[s][k][0].w;
+                            t1.x += tf[s][k][1].x; t1.y += tf[s][k][1].y; t1.z += tf[s][k][1].z; t1.w += tf[s][k][1].w;
+                        }
+                    y = mfma_f16(l2f[s], live ? f32x8_to_h8(t0, t1) : v8h{}, y);
                 }
             } else {
                 const int64_t chr = ch0 + fn_e * 16 + li, tokr = fm_e * 16 + li;
@@ -205,8 +224,11 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
 template <int FN, int FM, int U, int RS>
 static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)((a.n + FN * 16 - 1) / (FN * 16)));
+    constexpr int TK = RS > 0 && FN * FM <= 4 ? kMaxTSlices / RS : 1;  // partial sums of T the epilogue adds
     if (a.acc)
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true>), grid, dim3(256), 0, stream, a);
+    else if (TK > 1 && a.tks > 1)
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false, TK>), grid, dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
@@ -244,9 +266,7 @@ static hipError_t launch_decode(const DualArgs &a, hipStream_t stream) {
 // to the eight XCDs in turn): each XCD walks a contiguous range of tiles ordered in
 // groups of GM token tiles, so the CTAs an XCD runs at once share W and Q_X tiles in
 // that XCD's L2.
-constexpr int kStageRowBytes = 64;
 
-constexpr int kBlockBytes = 1024;  // 16 rows x 64 bytes
 // Block b runs on XCD b % 8 (the hardware deals CTAs out in turn). Give XCD x the
 // contiguous range of q + (x < rem) tiles starting at x q + min(x, rem), q = tiles / 8,
 // rem = tiles % 8: a bijection of [0, tiles) for any tile count.
@@ -274,9 +294,9 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
 // apart from the direct-to-LDS loads still in flight into other ring slots, and would
 // otherwise wait for all of those first. The offsets ride in the instructions'
 // 16-bit immediate field.
-template <int OFF>
+template <int OFF, int BLK>
 __device__ __forceinline__ void lds_read_4x4(uint32_t a, uint32_t b, v4i (&r)[8]) {
-    static_assert(OFF >= 0 && OFF + 3 * kBlockBytes < 65536, "ds_read immediate offset");
+    static_assert(OFF >= 0 && OFF + 3 * BLK < 65536, "ds_read immediate offset");
     asm volatile(
         "ds_read_b128 %0, %8 offset:%10\n\t"
         "ds_read_b128 %1, %8 offset:%11\n\t"
@@ -288,7 +308,7 @@ __device__ __forceinline__ void lds_read_4x4(uint32_t a, uint32_t b, v4i (&r)[8]
         "ds_read_b128 %7, %9 offset:%13\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7])
-        : "v"(a), "v"(b), "n"(OFF), "n"(OFF + kBlockBytes), "n"(OFF + 2 * kBlockBytes), "n"(OFF + 3 * kBlockBytes)
+        : "v"(a), "v"(b), "n"(OFF), "n"(OFF + BLK), "n"(OFF + 2 * BLK), "n"(OFF + 3 * BLK)
         : "memory");
 }
 
@@ -305,13 +325,16 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &
     (f(std::integral_constant<int, I>{}), ...);
 }
 
-template <int BN, int BM, int WN, int WM, int S, int GM, bool STORE_ACC>
+template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC>
 __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     constexpr int NT = WN * WM * 64;
     constexpr int FN = BN / (16 * WN), FM = BM / (16 * WM);
     constexpr int ROWS = BN + BM;
-    constexpr int STAGE_BYTES = ROWS * kStageRowBytes;
-    constexpr int DPT = ROWS * 4 / NT;  // 16-byte DMA loads per thread per stage
+    static_assert(RB == 64 || RB == 128, "bytes per row per stage");
+    constexpr int CPR = RB / 16;                // 16-byte chunks per row per stage
+    constexpr int BLK = 16 * RB;                // one block of 16 rows
+    constexpr int STAGE_BYTES = ROWS * RB;
+    constexpr int DPT = ROWS * CPR / NT;        // 16-byte DMA loads per thread per stage
     static_assert(ROWS * 4 % NT == 0 && FN >= 1 && FM >= 1, "tile shape");
     static_assert((S - 2) * DPT < 64, "outstanding loads fit vmcnt");
 
@@ -328,20 +351,21 @@ __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int t
     const int64_t tm = grp * GM + within % gm_here, tn = within / gm_here;
     const int64_t ch0 = tn * BN, tok0 = tm * BM;
     const int64_t kb = a.m / 2;
-    const int nst = (int)(a.m / 128);
+    const int nst = (int)(a.m / (2 * RB));  // m is a multiple of 2 RB
 
-    // this thread's DMA sources: slot q = j * NT + tid of each stage is position
-    // q % 8 of line (q % 64) / 8 of block q / 64. Each j lies wholly in the weight rows
-    // or wholly in the token rows, so its address is a uniform tile base (advanced by
-    // 64 bytes per stage) plus a 32-bit per-lane offset.
-    static_assert(NT % 64 == 0 && (BN * 4) % NT == 0, "each DMA group in one operand");
+    // this thread's DMA sources: slot q = j * NT + tid of each stage is 16-byte position
+    // q % 8 of 128-byte line (q % (16 CPR)) / 8 of block q / (16 CPR). Each j lies wholly
+    // in the weight rows or wholly in the token rows, so its address is a uniform tile
+    // base (advanced by RB bytes per stage) plus a 32-bit per-lane offset.
+    static_assert(NT % 64 == 0 && (BN * CPR) % NT == 0, "each DMA group in one operand");
     const uint8_t *wbase = a.qw + ch0 * kb, *xbase = a.qx + tok0 * kb;
     uint32_t off[DPT];
 #pragma unroll
     for (int j = 0; j < DPT; ++j) {
         const int q = j * NT + tid;
-        const int line = (q % 64) / 8, logical = (q % 8) ^ line;
-        const int row = (q / 64) * 16 + 2 * line + logical / 4, chunk = logical % 4;
+        const int line = (q % (16 * CPR)) / 8, logical = (q % 8) ^ (RB == 64 ? line : (line >> 1) & 7);
+        const int row = (q / (16 * CPR)) * 16 + (RB == 64 ? 2 * line + logical / 4 : line);
+        const int chunk = RB == 64 ? logical % 4 : logical;
         int64_t rel;  // row offset from the tile's first row, clamped into the operand
         if (row < BN) {
             const int64_t ch = ch0 + row;
@@ -353,15 +377,18 @@ __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int t
         off[j] = (uint32_t)(rel * kb + chunk * 16);
     }
     __shared__ __attribute__((aligned(16))) uint8_t ring[S * STAGE_BYTES];
+    // buffer loads straight to LDS: one resource per operand tile (raw, 32-bit element
+    // format; every offset stays inside the tile's clamped rows), the per-lane offset
+    // in a VGPR that never changes and the stage offset in an SGPR
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wbase), 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xbase), 0, 0x7fffffff, 0x00020000);
     auto issue = [&](int st, auto slot) {
         uint8_t *dst = ring + decltype(slot)::value * STAGE_BYTES;
-        const uint8_t *wst = wbase + (int64_t)st * kStageRowBytes, *xst = xbase + (int64_t)st * kStageRowBytes;
 #pragma unroll
-        for (int j = 0; j < DPT; ++j) {
-            const uint8_t *src = ((j * NT) / 4 < BN ? wst : xst) + off[j];
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
-                                             reinterpret_cast<void *>(dst + (j * NT + wave * kWave) * 16), 16, 0, 0);
-        }
+        for (int j = 0; j < DPT; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((j * NT) / CPR < BN ? rw : rx,
+                                                     (__attribute__((address_space(3))) void *)(dst + (j * NT + wave * kWave) * 16),
+                                                     16, (int)off[j], st * RB, 0, 0);
     };
 
     v4i acc[FN][FM];
@@ -370,12 +397,20 @@ __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int t
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = v4i{0, 0, 0, 0};
 
-    // this lane's operand addresses: FN weight blocks from rda, FM token blocks from rdb
+    // this lane's operand addresses, per MFMA k-step h of a stage: FN weight blocks from
+    // rda[h], FM token blocks from rdb[h]. Row li, chunk c of a block: with 64-byte rows,
+    // line li / 2 at position (4 (li % 2) + c) ^ (li / 2); with 128-byte rows, line li at
+    // position c ^ ((li / 2) % 8).
     static_assert(FN == 4 && FM == 4, "the stage reader loads four weight and four token blocks per wave");
-    // row li, chunk g of a block: line li / 2, logical position 4 (li % 2) + g
-    const uint32_t ring0 = lds_offset(ring) + (li / 2) * 128 + ((4 * (li % 2) + g) ^ (li / 2)) * 16;
-    const uint32_t rda = ring0 + (wn * (BN / WN) / 16) * kBlockBytes;
-    const uint32_t rdb = ring0 + ((BN + wm * (BM / WM)) / 16) * kBlockBytes;
+    constexpr int KS = RB / 64;  // MFMA k-steps per stage
+    uint32_t rda[KS], rdb[KS];
+#pragma unroll
+    for (int h = 0; h < KS; ++h) {
+        const uint32_t lane_off = RB == 64 ? (li / 2) * 128 + ((4 * (li % 2) + g) ^ (li / 2)) * 16
+                                           : li * 128 + ((4 * h + g) ^ ((li / 2) % 8)) * 16;
+        rda[h] = lds_offset(ring) + lane_off + (wn * (BN / WN) / 16) * BLK;
+        rdb[h] = lds_offset(ring) + lane_off + ((BN + wm * (BM / WM)) / 16) * BLK;
+    }
 
     // Step st issues stage st into slot st % S and consumes stage st - (S - 1). Every
     // step issues (past the last stage it loads the last stage again, into a slot no
@@ -392,20 +427,24 @@ __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int t
             }
             issue(st < nst ? st : nst - 1, u);
             if (c < 0) return;
-            v4i raw[8];
-            lds_read_4x4<((u + 1) % S) * STAGE_BYTES>(rda, rdb, raw);  // slot of stage c = st - (S - 1)
-            v4i alo[FN], ahi[FN], blo[FM], bhi[FM];
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) unpack16(raw[fn], alo[fn], ahi[fn]);
+            for (int h = 0; h < KS; ++h) {
+                constexpr int OFF = ((u + 1) % S) * STAGE_BYTES;  // slot of stage c
+                v4i raw[8];
+                lds_read_4x4<OFF, BLK>(rda[h], rdb[h], raw);
+                v4i alo[FN], ahi[FN], blo[FM], bhi[FM];
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) unpack16(raw[FN + fm], blo[fm], bhi[fm]);
+                for (int fn = 0; fn < FN; ++fn) unpack16(raw[fn], alo[fn], ahi[fn]);
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+                for (int fm = 0; fm < FM; ++fm) unpack16(raw[FN + fm], blo[fm], bhi[fm]);
 #pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    acc[fn][fm] = mfma_i8(alo[fn], blo[fm], acc[fn][fm]);
-                    acc[fn][fm] = mfma_i8(ahi[fn], bhi[fm], acc[fn][fm]);
-                }
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) {
+                        acc[fn][fm] = mfma_i8(alo[fn], blo[fm], acc[fn][fm]);
+                        acc[fn][fm] = mfma_i8(ahi[fn], bhi[fm], acc[fn][fm]);
+                    }
+            }
         });
     }
 
@@ -491,27 +530,44 @@ __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int t
     }
 }
 
-template <int BN, int BM, int WN, int WM, int S, int GM>
+template <int BN, int BM, int WN, int WM, int S, int GM, int RB>
 static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
     const int64_t tiles_n = (a.n + BN - 1) / BN, tiles_m = (a.b + BM - 1) / BM;
     const dim3 grid((unsigned)(tiles_n * tiles_m)), block(WN * WM * 64);
     if (a.acc)
-        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, true>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
+        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, true>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
     else
-        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, false>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
+        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, false>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
     return hipGetLastError();
+}
+
+// Decode tiles (FN x FM blocks of 16 channels x 16 tokens per CTA): wider channel
+// tiles read Q_X fewer times, as long as the grid still covers the chip (measured on
+// MI355X with HIP graphs, weights cold). false: many tokens, the LDS-ring kernel.
+// launch_dual_linear dispatches on the same conditions.
+static bool decode_shape(int64_t b, int64_t n, int &fn, int &fm) {
+    if (b <= 16) { fn = n >= 16384 ? 2 : 1; fm = 1; return true; }
+    if (b <= 32) { fn = n >= 8192 ? 4 : 1; fm = 2; return true; }
+    if (b <= 64) { fn = n >= 8192 ? 2 : 1; fm = 4; return true; }
+    return false;
 }
 
 hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream) {
     if (a.b == 0 || a.n == 0) return hipSuccess;
-    // decode tiles: wider channel tiles read Q_X fewer times, as long as the grid
-    // still covers the chip (measured on MI355X with HIP graphs, weights cold)
+    if (a.tks > 1 && (a.acc || a.lr4 || a.tks > dual_max_t_slices(a.b, a.n, a.r))) return hipErrorInvalidValue;
     if (a.b <= 16) return a.n >= 16384 ? launch_decode<2, 1, 8>(a, stream) : launch_decode<1, 1, 8>(a, stream);
     if (a.b <= 32) return a.n >= 8192 ? launch_decode<4, 2, 2>(a, stream) : launch_decode<1, 2, 4>(a, stream);
     if (a.b <= 64) return a.n >= 8192 ? launch_decode<2, 4, 2>(a, stream) : launch_decode<1, 4, 4>(a, stream);
     // many tokens: 128 x 128 tiles, 3-stage LDS ring, XCD groups of 8 token tiles
     // (the fastest exact variant measured on MI355X for the gate/up and down shapes)
-    return launch_pf<128, 128, 2, 2, 3, 8>(a, stream);
+    return launch_pf<128, 128, 2, 2, 3, 8, 64>(a, stream);
+}
+
+int dual_max_t_slices(int64_t b, int64_t n, int r) {
+    int fn, fm;
+    if (r == 0 || !decode_shape(b, n, fn, fm) || fn * fm > 4) return 1;  // the epilogue reads T whole
+    const int rs = r <= 32 ? 1 : r <= 64 ? 2 : r <= 128 ? 4 : 8;
+    return kMaxTSlices / rs;
 }
 
 }  // namespace twq

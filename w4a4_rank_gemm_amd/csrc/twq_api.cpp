@@ -31,6 +31,29 @@ bool valid_n(int64_t n) { return n >= 0 && n % 16 == 0 && n <= kMaxN; }
 bool valid_r(int64_t r) { return r >= 0 && r % 16 == 0 && r <= kMaxRank; }
 bool valid_r4(int64_t r) { return r >= 0 && r % 32 == 0 && r <= kMaxRank; }  // int4 low-rank variant
 
+// Workspace of twq_linear: Q_X, s_X, T and the partial sums of T, each 256-byte
+// aligned. With few tokens the dual launch adds the partial sums of T itself
+// (direct), so T is never written.
+struct LinearLayout {
+    twq::ActPlan plan;
+    bool direct;
+    size_t qx, sx, t, partials, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+LinearLayout linear_layout(int64_t b, int64_t m, int64_t n, int64_t r) {
+    LinearLayout L{};
+    L.plan = twq::plan_act(b, m, r);
+    L.direct = r > 0 && L.plan.mode == 1 && L.plan.ks > 1 && L.plan.ks <= twq::dual_max_t_slices(b, n, (int)r);
+    L.qx = 0;
+    L.sx = align256((size_t)(b * m / 2));
+    L.t = L.sx + align256((size_t)b * 4);
+    L.partials = L.t + (L.direct ? 0 : align256((size_t)(b * r) * 4));
+    L.total = L.partials + align256(L.plan.workspace_bytes);
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,6 +132,8 @@ twq_status twq_dual_linear(const void *qx, const float *sx, const void *qw, cons
     a.qw = static_cast<const uint8_t *>(qw);
     a.sw = sw;
     a.t = t;
+    a.tpart = t;
+    a.tks = 1;
     a.l2t = static_cast<const uint16_t *>(l2t);
     a.r = (int)r;
     a.y = static_cast<uint16_t *>(y);
@@ -129,6 +154,7 @@ twq_status twq_debug_residual_acc(const void *qx, const void *qw, int32_t *acc, 
     a.qx = static_cast<const uint8_t *>(qx);
     a.qw = static_cast<const uint8_t *>(qw);
     a.acc = acc;
+    a.tks = 1;
     a.b = b;
     a.m = m;
     a.n = n;
@@ -184,11 +210,64 @@ twq_status twq_dual_linear_lr4(const void *qx, const float *sx, const void *qw, 
     a.m = m;
     a.n = n;
     a.lr4 = 1;
+    a.tks = 1;
     a.qh = static_cast<const uint8_t *>(qh);
     a.sh = sh;
     a.ql2 = static_cast<const uint8_t *>(ql2);
     const hipError_t e = twq::launch_dual_linear(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_dual_linear_lr4");
+}
+
+size_t twq_linear_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r) {
+    if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return 0;
+    return linear_layout(b, m, n, r).total;
+}
+
+twq_status twq_linear(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t, int64_t r,
+                      void *y, int64_t b, int64_t m, int64_t n, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return TWQ_ERR_SHAPE;
+    if (b == 0 || n == 0) return TWQ_OK;
+    if (!x || !qw || !sw || !y) return TWQ_ERR_NULL;
+    if (r > 0 && (!l1t || !l2t)) return TWQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(qw) || !aligned16(sw) || !aligned16(y)) return TWQ_ERR_ALIGN;
+    if (r > 0 && (!aligned16(l1t) || !aligned16(l2t))) return TWQ_ERR_ALIGN;
+    const LinearLayout L = linear_layout(b, m, n, r);
+    if (!workspace || workspace_bytes < L.total) return TWQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return TWQ_ERR_ALIGN;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+
+    twq::ActArgs act{};
+    act.x = static_cast<const uint16_t *>(x);
+    act.b = b;
+    act.m = m;
+    act.qx = ws + L.qx;
+    act.sx = reinterpret_cast<float *>(ws + L.sx);
+    act.l1t = static_cast<const uint16_t *>(l1t);
+    act.r = (int)r;
+    act.t = reinterpret_cast<float *>(ws + L.t);
+    act.partials = reinterpret_cast<float *>(ws + L.partials);
+    act.keep_partials = L.direct;
+    hipError_t e = twq::launch_act(act, L.plan, st);
+    if (e != hipSuccess) return hip_fail(e, "twq_linear (activations)");
+
+    twq::DualArgs a{};
+    a.qx = act.qx;
+    a.sx = act.sx;
+    a.qw = static_cast<const uint8_t *>(qw);
+    a.sw = sw;
+    a.t = act.t;
+    a.tpart = L.direct ? act.partials : act.t;
+    a.tks = L.direct ? L.plan.ks : 1;
+    a.tstride = L.direct ? (int64_t)L.plan.fm * 16 * r : 0;
+    a.l2t = static_cast<const uint16_t *>(l2t);
+    a.r = (int)r;
+    a.y = static_cast<uint16_t *>(y);
+    a.b = b;
+    a.m = m;
+    a.n = n;
+    e = twq::launch_dual_linear(a, st);
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_linear");
 }
 
 }  // extern "C"

@@ -35,6 +35,7 @@ struct ActArgs {
     int r;
     float *t;
     float *partials;  // ks > 1: [ks][rows_pad][r], rows_pad = 64 row_tiles (mode 0) or 16 fm (mode 1)
+    int keep_partials;  // ks > 1: leave T as partial sums (the caller's dual launch adds them)
 };
 
 hipError_t launch_act(const ActArgs &a, const ActPlan &plan, hipStream_t stream);
@@ -50,9 +51,12 @@ struct DualArgs {
     const float *sx;
     const uint8_t *qw;
     const float *sw;
-    const float *t;
+    const float *t;    // [b][r]; the decode kernels read T through tpart instead
     const uint16_t *l2t;
     int r;
+    const float *tpart;  // T as tks partial sums: T[i][c] = sum_s tpart[s tstride + i r + c] (s in order)
+    int tks;
+    int64_t tstride;
     uint16_t *y;       // fp16 [b][n]
     int32_t *acc;      // int32 [b][n] instead of y (the exact integer sum)
     int64_t b, m, n;
@@ -63,6 +67,10 @@ struct DualArgs {
 };
 
 hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream);
+
+// Largest number of T partial-sum slices the dual launch for this shape adds itself
+// (1: it needs T whole).
+int dual_max_t_slices(int64_t b, int64_t n, int r);
 
 // ---- int4 low-rank variant ------------------------------------------------------------
 
