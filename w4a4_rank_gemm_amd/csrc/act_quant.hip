@@ -21,7 +21,7 @@ constexpr int kActThreads = 256;
 constexpr int kActMaxJ = 8;   // rows of up to 256 * 8 * 8 = 16384 fp16 stay in registers
 
 struct ActDev {
-    int mode;        // 0: tiles of 64 token rows x all ranks; 1: all tokens x 16 ranks x a K slice
+    int mode;        // 0: tiles of 128 token rows x all ranks; 1: all tokens x 16 ranks x a K slice
     int row_tile, ks, row_tiles, n_t_ctas;
     int fm;          // mode 1: token tiles of 16 (b <= 128)
     int nsl;         // CTAs per token row for the quantizer
@@ -40,13 +40,13 @@ __device__ __forceinline__ uint32_t absmax8_bits(const uint4 c, uint32_t mx) {
     return mx;
 }
 
-__device__ __forceinline__ uint32_t quant8(const uint4 c, float s) {
+__device__ __forceinline__ uint32_t quant8(const uint4 c, float s, float inv) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
     int q[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        q[2 * e] = quant_code(half_bits_to_float(w[e] & 0xFFFFu), s);
-        q[2 * e + 1] = quant_code(half_bits_to_float(w[e] >> 16), s);
+        q[2 * e] = quant_code_fast(half_bits_to_float(w[e] & 0xFFFFu), s, inv);
+        q[2 * e + 1] = quant_code_fast(half_bits_to_float(w[e] >> 16), s, inv);
     }
     return pack8(q);
 }
@@ -82,66 +82,114 @@ __device__ void quantize_row(const ActArgs &a, int64_t i, int sl, int nsl, uint3
     for (int w = 1; w < kActThreads / kWave; ++w) mx = mx > red[w] ? mx : red[w];
     const float amax = half_bits_to_float(mx);
     const float s = amax / kQMax;  // correctly rounded binary32 division
+    const float inv = 1.0f / s;    // only used when amax > 0
     if (tid == 0 && sl == 0) a.sx[i] = s;
     if (cached) {
 #pragma unroll
         for (int j = 0; j < kActMaxJ; ++j) {
             const int64_t c = tid + (int64_t)j * kActThreads;
-            if (c >= c_lo && c < c_hi) qr[c] = amax == 0.0f ? 0u : quant8(v[j], s);
+            if (c >= c_lo && c < c_hi) qr[c] = amax == 0.0f ? 0u : quant8(v[j], s, inv);
         }
     } else {
-        for (int64_t c = c_lo + tid; c < c_hi; c += kActThreads) qr[c] = amax == 0.0f ? 0u : quant8(xr[c], s);
+        for (int64_t c = c_lo + tid; c < c_hi; c += kActThreads) qr[c] = amax == 0.0f ? 0u : quant8(xr[c], s, inv);
     }
 }
 
-// T tile for many tokens: rows [64 rt, 64 rt + 64) (one 16-row slab per wave) x all
-// r = 16 NT ranks, over K slice ks. A = L1^T rows (16 ranks), B = X rows (16
-// tokens), so lane (li, g) ends with ranks 4g..4g+3 of token li in each rank tile.
-// U steps of 32 are loaded before any is multiplied. With several K slices the
-// partial sums go to partials[ks] and a second kernel adds them in slice order.
-template <int NT>
-__device__ void t_rows(const ActArgs &a, const ActDev &p, int tb) {
-    constexpr int U = NT <= 4 ? 4 : (NT <= 8 ? 2 : 1);
-    const int rt = tb / p.ks, ks = tb % p.ks;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+// T tile for many tokens: tokens [128 tm, 128 tm + 128) x all r = 16 NR ranks over K
+// slice ks, in steps of 32 (64 bytes of fp16 per row). The step's 128 X rows and its
+// L1^T rows (NR blocks of 16, padded to a multiple of four blocks with clamped rows)
+// go through a three-slot LDS ring filled by direct-to-LDS buffer loads, laid out as
+// the prefill main loop's ring: 16-row blocks, rows 2s and 2s + 1 sharing 128-byte
+// line s with the 16-byte chunk index XORed by s, which makes the loads coalesce and
+// the operand reads conflict-free. X rows are read from HBM once and L1 rows once per
+// CTA. Wave w owns tokens [32 w, 32 w + 32) x all ranks: A = L1^T block (16 ranks),
+// B = X block (16 tokens), so lane (li, g) ends with ranks 4g..4g+3 of token li.
+template <int NR>
+__device__ void t_tiles(const ActArgs &a, const ActDev &p, int tb, uint8_t *ring) {
+    constexpr int BM = 128, NRP = (NR + 3) / 4 * 4, ROWS = BM + 16 * NRP;
+    constexpr int S = 3, BLK = 1024, STAGE = ROWS * 64, DPT = ROWS * 4 / kActThreads;
+    static_assert(ROWS * 4 % kActThreads == 0 && BM * 4 % kActThreads == 0, "DMA groups");
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int li = lane & 15, g = lane >> 4;
-    const int64_t kslice = a.m / p.ks;
-    const int64_t kbeg = ks * kslice, kend = kbeg + kslice;
-    const int64_t row = (int64_t)rt * 64 + wave * 16 + li;
-    const bool rv = row < a.b;
-    const uint16_t *xp = a.x + (rv ? row : 0) * a.m + g * 8;
-    const uint16_t *lp = a.l1t + (int64_t)li * a.m + g * 8;
+    const int tm = tb / p.ks, ks = tb % p.ks;
+    const int64_t kslice = a.m / p.ks, kbeg = ks * kslice;
+    const int nst = (int)(kslice / 32);
+    const int64_t tok0 = (int64_t)tm * BM;
 
-    v4f acc[NT];
+    // slot q of a stage: position q % 8 of line (q % 64) / 8 of block q / 64
+    const uint8_t *xb = reinterpret_cast<const uint8_t *>(a.x + tok0 * a.m + kbeg);
+    const uint8_t *lb = reinterpret_cast<const uint8_t *>(a.l1t + kbeg);
+    uint32_t off[DPT];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) acc[tt] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int64_t k = kbeg; k < kend; k += 32 * U) {
-        v8h xb[U], la[U][NT];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t kk = k + 32 * u;
-            const bool ok = kk < kend;
-            xb[u] = (ok && rv) ? load_h8(xp + kk) : v8h{};
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) la[u][tt] = ok ? load_h8(lp + (int64_t)tt * 16 * a.m + kk) : v8h{};
+    for (int j = 0; j < DPT; ++j) {
+        const int q = j * kActThreads + tid;
+        const int line = (q % 64) / 8, logical = (q % 8) ^ line;
+        const int row = (q / 64) * 16 + 2 * line + logical / 4, chunk = logical % 4;
+        int64_t rel;
+        if (row < BM) {
+            const int64_t tok = tok0 + row;
+            rel = (tok < a.b ? tok : a.b - 1) - tok0;
+        } else {
+            const int rank = row - BM;
+            rel = rank < a.r ? rank : a.r - 1;
         }
-        __builtin_amdgcn_sched_barrier(0);  // every load of the batch in flight before the first use
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma_f16(la[u][tt], xb[u], acc[tt]);
+        off[j] = (uint32_t)(rel * a.m * 2 + chunk * 16);
     }
-    if (p.ks == 1) {
-        if (rv) {
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xb), 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(lb), 0, 0x7fffffff, 0x00020000);
+    auto issue = [&](int st, auto slot) {
+        uint8_t *dst = ring + decltype(slot)::value * STAGE;
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) *reinterpret_cast<v4f *>(a.t + row * a.r + tt * 16 + 4 * g) = acc[tt];
+        for (int j = 0; j < DPT; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((j * kActThreads) / 4 < BM ? rx : rl,
+                                                     (__attribute__((address_space(3))) void *)(dst + (j * kActThreads + wave * kWave) * 16),
+                                                     16, (int)off[j], st * 64, 0, 0);
+    };
+
+    v4f acc[NR][2];
+#pragma unroll
+    for (int tt = 0; tt < NR; ++tt) acc[tt][0] = acc[tt][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    // row li, chunk g of a block: line li / 2, logical position 4 (li % 2) + g
+    const uint32_t lane_off = lds_offset(ring) + (li / 2) * 128 + ((4 * (li % 2) + g) ^ (li / 2)) * 16;
+    const uint32_t rdx = lane_off + 2 * wave * BLK, rdl = lane_off + (BM / 16) * BLK;
+
+    for (int s0 = 0; s0 < nst + S - 1; s0 += S) {
+        static_for(std::make_integer_sequence<int, S>{}, [&](auto u) {
+            const int st = s0 + u, c = st - (S - 1);
+            if (c >= nst) return;
+            if (c >= 0) {
+                wait_vmcnt<(S - 2) * DPT>();
+                stage_barrier();  // stage c landed for every thread; stage c - 1 consumed by every wave
+            }
+            issue(st < nst ? st : nst - 1, u);
+            if (c < 0) return;
+            constexpr int OFF = ((u + 1) % S) * STAGE;  // slot of stage c
+            v4i xr[2];
+            lds_read_2<OFF, BLK>(rdx, xr);
+            static_for(std::make_integer_sequence<int, NRP / 4>{}, [&](auto q4) {
+                constexpr int t0 = 4 * decltype(q4)::value;
+                v4i lr[4];
+                lds_read_4<OFF + t0 * BLK, BLK>(rdl, lr);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (t0 + k < NR) {
+#pragma unroll
+                        for (int f = 0; f < 2; ++f)
+                            acc[t0 + k][f] = mfma_f16(__builtin_bit_cast(v8h, lr[k]), __builtin_bit_cast(v8h, xr[f]), acc[t0 + k][f]);
+                    }
+            });
+        });
+    }
+
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const int64_t row = tok0 + 32 * wave + 16 * f + li;
+        float *dst = p.ks == 1 ? a.t + row * a.r : a.partials + ((int64_t)ks * p.row_tiles * BM + row) * a.r;
+        if (p.ks > 1 || row < a.b) {
+#pragma unroll
+            for (int tt = 0; tt < NR; ++tt) *reinterpret_cast<v4f *>(dst + tt * 16 + 4 * g) = acc[tt][f];
         }
-        return;
     }
-    const int64_t prow_stride = (int64_t)p.row_tiles * 64 * a.r;
-    float *dst = a.partials + ks * prow_stride + row * a.r + 4 * g;
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) *reinterpret_cast<v4f *>(dst + tt * 16) = acc[tt];
 }
 
 // T partial for few tokens: all b tokens (FM tiles of 16) x ranks [16 rt, 16 rt + 16)
@@ -207,16 +255,17 @@ __device__ void t_slices(const ActArgs &a, const ActDev &p, int tb, float *lds) 
     }
 }
 
-// Many tokens (MODE 0): T partials by t_rows<NT>. Few tokens (MODE 1): T partials by
-// t_slices<NT = FM>. The remaining CTAs quantize, nsl CTAs per token row.
+// Many tokens (MODE 0): T partials by t_tiles<NT = r / 16>. Few tokens (MODE 1): T
+// partials by t_slices<NT = FM>. The remaining CTAs quantize, nsl CTAs per token row.
 template <int MODE, int NT>
 __global__ __launch_bounds__(kActThreads) void act_kernel(ActArgs a, ActDev p) {
     __shared__ float lds[MODE == 1 ? 3 * NT * kWave * 4 : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[MODE == 0 ? 3 * (128 + 16 * ((NT + 3) / 4 * 4)) * 64 : 16];
     __shared__ uint32_t red[kActThreads / kWave];
     const int64_t bid = blockIdx.x;
     if (bid < p.n_t_ctas) {
         if constexpr (MODE == 0)
-            t_rows<NT>(a, p, (int)bid);
+            t_tiles<NT>(a, p, (int)bid, ring);
         else
             t_slices<NT>(a, p, (int)bid, lds);
     } else {
@@ -259,14 +308,14 @@ ActPlan plan_act(int64_t b, int64_t m, int64_t r) {
     pl.nsl = 1;
     if (b == 0) return pl;
     if (b > 128) {
-        // many tokens: 64-row tiles x all ranks; K slices until about 512 CTAs,
-        // keeping slices of at least 512
+        // many tokens: 128-row tiles x all ranks; K slices (steps of 32, at least 512
+        // long) until about 256 CTAs
         pl.mode = 0;
-        pl.row_tile = 64;
-        pl.row_tiles = (int)((b + 63) / 64);
+        pl.row_tile = 128;
+        pl.row_tiles = (int)((b + 127) / 128);
         int64_t ks = 1;
         if (r > 0)
-            while ((int64_t)pl.row_tiles * ks < 512 && m / (ks * 2) >= 512 && m % (ks * 2 * 32) == 0) ks *= 2;
+            while ((int64_t)pl.row_tiles * ks < 256 && m / (ks * 2) >= 512 && m % (ks * 2 * 32) == 0) ks *= 2;
         pl.ks = (int)ks;
     } else {
         // few tokens: every token x one 16-rank tile x one K slice per CTA, slices of
@@ -286,7 +335,7 @@ ActPlan plan_act(int64_t b, int64_t m, int64_t r) {
         pl.nsl = (int)nsl;
     }
     if (r > 0 && pl.ks > 1) {
-        const int64_t rows_pad = pl.mode == 0 ? (int64_t)pl.row_tiles * 64 : (int64_t)pl.fm * 16;
+        const int64_t rows_pad = pl.mode == 0 ? (int64_t)pl.row_tiles * 128 : (int64_t)pl.fm * 16;
         pl.workspace_bytes = (size_t)pl.ks * rows_pad * r * sizeof(float);
     }
     return pl;
@@ -343,7 +392,7 @@ hipError_t launch_act(const ActArgs &a, const ActPlan &pl, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.r == 0 || pl.ks == 1 || a.keep_partials) return e;
     const int64_t n4 = a.b * a.r / 4;
-    const int64_t rows_pad = pl.mode == 0 ? (int64_t)pl.row_tiles * 64 : (int64_t)pl.fm * 16;
+    const int64_t rows_pad = pl.mode == 0 ? (int64_t)pl.row_tiles * 128 : (int64_t)pl.fm * 16;
     hipLaunchKernelGGL(t_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a.partials, a.b,
                        rows_pad, a.r, pl.ks, a.t);
     return hipGetLastError();

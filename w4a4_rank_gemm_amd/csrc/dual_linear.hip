@@ -275,56 +275,6 @@ __host__ __device__ __forceinline__ int64_t xcd_order(int64_t bid, int64_t ntile
     return x * q + (x < rem ? x : rem) + j;
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    // vmcnt = N, expcnt and lgkmcnt left at their maxima (not waited on)
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// LDS byte offset of a pointer into __shared__ memory.
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// The eight operand reads of one stage: four consecutive 1 KB blocks from address a
-// and four from address b (each plus OFF), completed before returning (the wait is
-// part of the same asm statement, so no output register is live while its load is in
-// flight). Written as one statement because the compiler cannot tell these reads
-// apart from the direct-to-LDS loads still in flight into other ring slots, and would
-// otherwise wait for all of those first. The offsets ride in the instructions'
-// 16-bit immediate field.
-template <int OFF, int BLK>
-__device__ __forceinline__ void lds_read_4x4(uint32_t a, uint32_t b, v4i (&r)[8]) {
-    static_assert(OFF >= 0 && OFF + 3 * BLK < 65536, "ds_read immediate offset");
-    asm volatile(
-        "ds_read_b128 %0, %8 offset:%10\n\t"
-        "ds_read_b128 %1, %8 offset:%11\n\t"
-        "ds_read_b128 %2, %8 offset:%12\n\t"
-        "ds_read_b128 %3, %8 offset:%13\n\t"
-        "ds_read_b128 %4, %9 offset:%10\n\t"
-        "ds_read_b128 %5, %9 offset:%11\n\t"
-        "ds_read_b128 %6, %9 offset:%12\n\t"
-        "ds_read_b128 %7, %9 offset:%13\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7])
-        : "v"(a), "v"(b), "n"(OFF), "n"(OFF + BLK), "n"(OFF + 2 * BLK), "n"(OFF + 3 * BLK)
-        : "memory");
-}
-
-// Workgroup barrier without the memory fence __syncthreads adds (which waits for every
-// outstanding load); callers first wait for their own loads of the stage they need.
-__device__ __forceinline__ void stage_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-template <int... I, class F>
-__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &&f) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC>
 __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     constexpr int NT = WN * WM * 64;

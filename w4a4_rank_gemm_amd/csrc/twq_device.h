@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <utility>
 #include <stdint.h>
 
 namespace twq {
@@ -21,6 +22,21 @@ __device__ __forceinline__ int quant_code(float v, float s) {
 #pragma clang fp contract(off)
     float ratio = v / s;
     float r = __builtin_rintf(ratio);
+    r = __builtin_fminf(__builtin_fmaxf(r, -kQMax), kQMax);
+    return (int)r;
+}
+
+// quant_code(v, s) without a division per element, given inv = fl32(1 / s) and
+// |v| <= 7 s (every element of the vector s was taken from). t = fl32(v inv) is
+// within 9e-7 of v / s (two roundings of relative size 2^-24 on a ratio of at most
+// 7.5), and the correctly rounded fl32(v / s) within 4.5e-7, so their nearest
+// integers can differ only if a half-integer lies within 1.4e-6 of t. Only then
+// (|t - rint(t)| >= 0.5 - 2^-18) is the division done.
+__device__ __forceinline__ int quant_code_fast(float v, float s, float inv) {
+#pragma clang fp contract(off)
+    float t = v * inv;
+    float r = __builtin_rintf(t);
+    if (__builtin_fabsf(t - r) >= 0.5f - 0x1p-18f) r = __builtin_rintf(v / s);
     r = __builtin_fminf(__builtin_fmaxf(r, -kQMax), kQMax);
     return (int)r;
 }
@@ -94,6 +110,89 @@ __device__ __forceinline__ v8h f32x8_to_h8(const float4 a, const float4 b) {
     r[0] = (_Float16)a.x; r[1] = (_Float16)a.y; r[2] = (_Float16)a.z; r[3] = (_Float16)a.w;
     r[4] = (_Float16)b.x; r[5] = (_Float16)b.y; r[6] = (_Float16)b.z; r[7] = (_Float16)b.w;
     return r;
+}
+
+// ---- LDS rings filled by direct-to-LDS loads (the prefill main loop and the
+// many-token first low-rank product) ----
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // vmcnt = N, expcnt and lgkmcnt left at their maxima (not waited on)
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// LDS byte offset of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// The eight operand reads of one stage: four consecutive 1 KB blocks from address a
+// and four from address b (each plus OFF), completed before returning (the wait is
+// part of the same asm statement, so no output register is live while its load is in
+// flight). Written as one statement because the compiler cannot tell these reads
+// apart from the direct-to-LDS loads still in flight into other ring slots, and would
+// otherwise wait for all of those first. The offsets ride in the instructions'
+// 16-bit immediate field.
+template <int OFF, int BLK>
+__device__ __forceinline__ void lds_read_4x4(uint32_t a, uint32_t b, v4i (&r)[8]) {
+    static_assert(OFF >= 0 && OFF + 3 * BLK < 65536, "ds_read immediate offset");
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%10\n\t"
+        "ds_read_b128 %1, %8 offset:%11\n\t"
+        "ds_read_b128 %2, %8 offset:%12\n\t"
+        "ds_read_b128 %3, %8 offset:%13\n\t"
+        "ds_read_b128 %4, %9 offset:%10\n\t"
+        "ds_read_b128 %5, %9 offset:%11\n\t"
+        "ds_read_b128 %6, %9 offset:%12\n\t"
+        "ds_read_b128 %7, %9 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7])
+        : "v"(a), "v"(b), "n"(OFF), "n"(OFF + BLK), "n"(OFF + 2 * BLK), "n"(OFF + 3 * BLK)
+        : "memory");
+}
+
+// Workgroup barrier without the memory fence __syncthreads adds (which waits for every
+// outstanding load); callers first wait for their own loads of the stage they need.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int... I, class F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &&f) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+// Two 16-byte LDS reads of consecutive blocks at address a (plus OFF), completed
+// before returning, for the same reason and in the same way as lds_read_4x4.
+template <int OFF, int BLK>
+__device__ __forceinline__ void lds_read_2(uint32_t a, v4i (&r)[2]) {
+    static_assert(OFF >= 0 && OFF + BLK < 65536, "ds_read immediate offset");
+    asm volatile(
+        "ds_read_b128 %0, %2 offset:%3\n\t"
+        "ds_read_b128 %1, %2 offset:%4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(r[0]), "=v"(r[1])
+        : "v"(a), "n"(OFF), "n"(OFF + BLK)
+        : "memory");
+}
+
+// Four 16-byte LDS reads of consecutive blocks at address a (plus OFF), completed
+// before returning, for the same reason and in the same way as lds_read_4x4.
+template <int OFF, int BLK>
+__device__ __forceinline__ void lds_read_4(uint32_t a, v4i (&r)[4]) {
+    static_assert(OFF >= 0 && OFF + 3 * BLK < 65536, "ds_read immediate offset");
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%5\n\t"
+        "ds_read_b128 %1, %4 offset:%6\n\t"
+        "ds_read_b128 %2, %4 offset:%7\n\t"
+        "ds_read_b128 %3, %4 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3])
+        : "v"(a), "n"(OFF), "n"(OFF + BLK), "n"(OFF + 2 * BLK), "n"(OFF + 3 * BLK)
+        : "memory");
 }
 
 }  // namespace twq

@@ -10,18 +10,18 @@ namespace twq {
 // ---- activation quantizer + first low-rank product ------------------------------
 
 // How the activation launch is split. T = X L1 is cut into ks K slices whose partial
-// sums (in the workspace) a second kernel adds. Many tokens (mode 0): tiles of 64
-// token rows x all ranks, one 16-row slab per wave. Few tokens (mode 1): every
-// token x one 16-rank tile per CTA, the four waves splitting the CTA's slice. The
-// quantizer takes nsl CTAs per token row.
+// sums (in the workspace) a second kernel adds. Many tokens (mode 0): tiles of 128
+// token rows x all ranks staged through an LDS ring, 32 rows per wave. Few tokens
+// (mode 1): every token x one 16-rank tile per CTA, the four waves splitting the
+// CTA's slice. The quantizer takes nsl CTAs per token row.
 struct ActPlan {
     int mode;        // 0 or 1, as above
     int fm;          // mode 1: token tiles of 16
-    int row_tile;    // token rows of the partial-sum layout per tile: 64 (mode 0) or 16 fm (mode 1)
+    int row_tile;    // token rows of the partial-sum layout per tile: 128 (mode 0) or 16 fm (mode 1)
     int ks;          // K slices; 1 means T is written directly
-    int row_tiles;   // mode 0: ceil(b / 64) row tiles; mode 1: r / 16 rank tiles
+    int row_tiles;   // mode 0: ceil(b / 128) row tiles; mode 1: r / 16 rank tiles
     int nsl;         // CTAs per token row for the quantizer
-    size_t workspace_bytes;  // partial sums of T: ks slices of [row_tiles * 64 or 16 fm][r] floats
+    size_t workspace_bytes;  // partial sums of T: ks slices of [row_tiles * 128 or 16 fm][r] floats
 };
 
 ActPlan plan_act(int64_t b, int64_t m, int64_t r);
@@ -34,7 +34,7 @@ struct ActArgs {
     const uint16_t *l1t;
     int r;
     float *t;
-    float *partials;  // ks > 1: [ks][rows_pad][r], rows_pad = 64 row_tiles (mode 0) or 16 fm (mode 1)
+    float *partials;  // ks > 1: [ks][rows_pad][r], rows_pad = 128 row_tiles (mode 0) or 16 fm (mode 1)
     int keep_partials;  // ks > 1: leave T as partial sums (the caller's dual launch adds them)
 };
 
