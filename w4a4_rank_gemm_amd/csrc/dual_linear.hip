@@ -275,6 +275,94 @@ __host__ __device__ __forceinline__ int64_t xcd_order(int64_t bid, int64_t ntile
     return x * q + (x < rem ? x : rem) + j;
 }
 
+// Epilogue of the many-token kernels for a wave's FN x FM tiles of 16 x 16, the wave
+// at (wn, wm) of a BN x BM CTA tile at (ch0, tok0): dequantize, add the low-rank
+// branch, store fp16 (or the exact integer sum).
+template <int BN, int BM, int WN, int WM, bool STORE_ACC, int FN, int FM>
+__device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM], int64_t ch0, int64_t tok0, int wn, int wm,
+                                            int li, int g) {
+    // lane (li, g), register v of tile (fn, fm) holds channel ch_base + 4g + v, token tok_base + li
+    if constexpr (STORE_ACC) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + 4 * g;
+                const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
+                if (ch < a.n && tok < a.b) *reinterpret_cast<v4i *>(a.acc + tok * a.n + ch) = acc[fn][fm] >> 8;
+            }
+    } else {
+        float sxv[FM];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
+            sxv[fm] = a.sx[tok < a.b ? tok : a.b - 1];
+        }
+        v4f y[FN][FM];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + 4 * g;
+            const float4 sw4 = *reinterpret_cast<const float4 *>(a.sw + (ch < a.n ? ch : a.n - 4));
+            const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) y[fn][fm][v] = (sxv[fm] * swv[v]) * (float)(acc[fn][fm][v] >> 8);
+        }
+        if (a.lr4) {
+            // int4 low-rank branch: y += s_H (Q_H Q_L2^T)
+            if (a.r > 0) {
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) {
+                        const int64_t chr = ch0 + wn * (BN / WN) + fn * 16 + li;
+                        const int64_t tokr = tok0 + wm * (BM / WM) + fm * 16 + li;
+                        const v4i acc2 = lr4_tile(a, chr, tokr, g);
+                        const float shv = a.sh[tokr < a.b ? tokr : a.b - 1];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) y[fn][fm][v] += shv * (float)(acc2[v] >> 8);
+                    }
+            }
+        }
+        // fp16 low-rank branch: y += L2^T (channels x ranks) . T^T (ranks x tokens)
+        for (int k0 = 0; k0 < (a.lr4 ? 0 : a.r); k0 += 32) {
+            const int rank = k0 + g * 8;
+            const bool live = rank < a.r;  // r is a multiple of 16: live means rank + 8 <= r
+            const int rk = live ? rank : 0;
+            v8h la[FN], tb[FM];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + li;
+                la[fn] = load_h8(a.l2t + (ch < a.n ? ch : a.n - 1) * a.r + rk);
+            }
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
+                const float4 *tp = reinterpret_cast<const float4 *>(a.t + (tok < a.b ? tok : a.b - 1) * a.r + rk);
+                tb[fm] = live ? f32x8_to_h8(tp[0], tp[1]) : v8h{};
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) y[fn][fm] = mfma_f16(la[fn], tb[fm], y[fn][fm]);
+        }
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + 4 * g;
+                const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
+                if (ch < a.n && tok < a.b) {
+                    v4h o;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) o[v] = (_Float16)y[fn][fm][v];
+                    *reinterpret_cast<v4h *>(a.y + tok * a.n + ch) = o;
+                }
+            }
+    }
+}
+
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC>
 __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     constexpr int NT = WN * WM * 64;
@@ -398,86 +486,7 @@ __global__ __launch_bounds__(WN * WM * 64) void dual_linear_pf(DualArgs a, int t
         });
     }
 
-    // lane (li, g), register v of tile (fn, fm) holds channel ch_base + 4g + v, token tok_base + li
-    if constexpr (STORE_ACC) {
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + 4 * g;
-                const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
-                if (ch < a.n && tok < a.b) *reinterpret_cast<v4i *>(a.acc + tok * a.n + ch) = acc[fn][fm] >> 8;
-            }
-    } else {
-        float sxv[FM];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
-            sxv[fm] = a.sx[tok < a.b ? tok : a.b - 1];
-        }
-        v4f y[FN][FM];
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + 4 * g;
-            const float4 sw4 = *reinterpret_cast<const float4 *>(a.sw + (ch < a.n ? ch : a.n - 4));
-            const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) y[fn][fm][v] = (sxv[fm] * swv[v]) * (float)(acc[fn][fm][v] >> 8);
-        }
-        if (a.lr4) {
-            // int4 low-rank branch: y += s_H (Q_H Q_L2^T)
-            if (a.r > 0) {
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-                    for (int fm = 0; fm < FM; ++fm) {
-                        const int64_t chr = ch0 + wn * (BN / WN) + fn * 16 + li;
-                        const int64_t tokr = tok0 + wm * (BM / WM) + fm * 16 + li;
-                        const v4i acc2 = lr4_tile(a, chr, tokr, g);
-                        const float shv = a.sh[tokr < a.b ? tokr : a.b - 1];
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) y[fn][fm][v] += shv * (float)(acc2[v] >> 8);
-                    }
-            }
-        }
-        // fp16 low-rank branch: y += L2^T (channels x ranks) . T^T (ranks x tokens)
-        for (int k0 = 0; k0 < (a.lr4 ? 0 : a.r); k0 += 32) {
-            const int rank = k0 + g * 8;
-            const bool live = rank < a.r;  // r is a multiple of 16: live means rank + 8 <= r
-            const int rk = live ? rank : 0;
-            v8h la[FN], tb[FM];
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + li;
-                la[fn] = load_h8(a.l2t + (ch < a.n ? ch : a.n - 1) * a.r + rk);
-            }
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
-                const float4 *tp = reinterpret_cast<const float4 *>(a.t + (tok < a.b ? tok : a.b - 1) * a.r + rk);
-                tb[fm] = live ? f32x8_to_h8(tp[0], tp[1]) : v8h{};
-            }
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) y[fn][fm] = mfma_f16(la[fn], tb[fm], y[fn][fm]);
-        }
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + 4 * g;
-                const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
-                if (ch < a.n && tok < a.b) {
-                    v4h o;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) o[v] = (_Float16)y[fn][fm][v];
-                    *reinterpret_cast<v4h *>(a.y + tok * a.n + ch) = o;
-                }
-            }
-    }
+    pf_epilogue<BN, BM, WN, WM, STORE_ACC>(a, acc, ch0, tok0, wn, wm, li, g);
 }
 
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB>
