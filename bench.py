@@ -48,6 +48,18 @@ def dual_linear_bytes(b, m, n, r):
     return b * m // 2 + 4 * b + m * n // 2 + 4 * n + 4 * b * r + 2 * n * r + 2 * b * n
 
 
+def call_bytes_lr4(b, m, n, r):
+    """Compulsory HBM bytes of one call with the int4 low-rank branch: X fp16, Q_W, s_W,
+    Q_L1 and Q_L2 (4-bit), c, Y fp16."""
+    return 2 * b * m + m * n // 2 + 4 * n + r * (m + n) // 2 + 4 * r + 2 * b * n
+
+
+def dual_linear_lr4_bytes(b, m, n, r):
+    """Algorithmic bytes of one twq_dual_linear_lr4 launch: Q_X, s_X, Q_W, s_W, Q_H, s_H and
+    Q_L2 read once, Y written once."""
+    return b * m // 2 + 4 * b + m * n // 2 + 4 * n + b * r // 2 + 4 * b + n * r // 2 + 2 * b * n
+
+
 KERNEL_SOURCES = ("w4a4_rank_gemm_amd/csrc/dual_linear.hip", "w4a4_rank_gemm_amd/csrc/twq_device.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dual_linear_traffic.json")
 
@@ -81,7 +93,7 @@ def lowrank_storage_ratio(m, n, r):
     return 2 * r * (m + n) / (m * n / 2)
 
 
-def _cpu_baseline(d, budget_s=12.0):
+def _cpu_baseline(d, budget_s=12.0, lr4=False):
     """The oracle (plain C, OpenMP) on the host: per-call work with weights pre-quantized."""
     import numpy as np
 
@@ -90,13 +102,17 @@ def _cpu_baseline(d, budget_s=12.0):
     b, m = x.shape
     n, r = w.shape[0], l1t.shape[0]
     qw, _, sw = oracle.quantize_weight(w)  # offline packing, not timed
+    lq = oracle.quantize_lowrank(l1t, l2t) if (lr4 and r) else None
     calls = 0
     t0 = time.perf_counter()
     while True:
         qx, _, sx = oracle.quantize_act(x)
         acc = oracle.residual_acc(qx, qw)
         y = sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] * acc
-        if r:
+        if r and lr4:
+            rq = oracle.lowrank_requant(qx, sx, lq["ql1"], lq["c"])
+            y += rq["sh"].astype(np.float64)[:, None] * oracle.residual_acc(rq["qh"], lq["ql2"])
+        elif r:
             y += oracle.lowrank_out(oracle.lowrank_t(x, l1t), l2t)
         calls += 1
         el = time.perf_counter() - t0
@@ -117,6 +133,9 @@ def main():
     ap.add_argument("--config", default="o_proj_decode")
     ap.add_argument("--path", choices=("linear", "split"), default="linear",
                     help="linear: one twq_linear call per step; split: twq_quantize_act + twq_dual_linear")
+    ap.add_argument("--lowrank", choices=("fp16", "int4"), default="fp16",
+                    help="fp16: the fp16 low-rank branch; int4: twq_quantize_act + twq_lowrank_requant "
+                         "+ twq_dual_linear_lr4 with 4-bit L1, L2 and H")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate over (0: auto)")
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
@@ -142,7 +161,10 @@ def main():
     print(f"# generating {args.config}: b={b} m={m} n={n} r={r}", file=sys.stderr, flush=True)
     d = synth.make_layer(cfg)
 
-    per_copy = call_bytes(b, m, n, r)
+    lr4 = args.lowrank == "int4"
+    if lr4 and args.path != "linear":
+        ap.error("--lowrank int4 has one call sequence; leave --path at its default")
+    per_copy = call_bytes_lr4(b, m, n, r) if lr4 else call_bytes(b, m, n, r)
     copies = args.copies or max(1, math.ceil(ROTATE_BYTES / per_copy))
     x0 = torch.from_numpy(d["x"]).to(dev)
     w0 = torch.from_numpy(d["w_res"]).to(dev)
@@ -150,16 +172,25 @@ def main():
     l20 = torch.from_numpy(d["l2t"]).to(dev) if r else None
     qw0, sw0 = twq.pack_weight(w0)
     del w0
+    lp0 = twq.pack_lowrank_int4(l10, l20) if (lr4 and r) else None
     sets = []
     for c in range(copies):
-        sets.append({
+        s_ = {
             "x": x0.clone(), "qw": qw0.clone(), "sw": sw0.clone(),
-            "l1t": l10.clone() if r else None, "l2t": l20.clone() if r else None,
+            "l1t": l10.clone() if (r and not lr4) else None, "l2t": l20.clone() if (r and not lr4) else None,
             "qx": torch.empty((b, m // 2), dtype=torch.uint8, device=dev),
             "sx": torch.empty((b,), dtype=torch.float32, device=dev),
-            "t": torch.empty((b, r), dtype=torch.float32, device=dev) if r else None,
+            "t": torch.empty((b, r), dtype=torch.float32, device=dev) if (r and not lr4) else None,
             "y": torch.empty((b, n), dtype=torch.float16, device=dev),
-        })
+        }
+        if lr4:
+            s_.update({"ql1": lp0["ql1"].clone() if r else None, "c": lp0["c"].clone() if r else None,
+                       "ql2": lp0["ql2"].clone() if r else None,
+                       "h": torch.empty((b, r), dtype=torch.int32, device=dev) if r else None,
+                       "qh": torch.empty((b, r // 2), dtype=torch.uint8, device=dev) if r else None,
+                       "sh": torch.empty((b,), dtype=torch.float32, device=dev) if r else None})
+        sets.append(s_)
+    del lp0
     L = twq.lib()
     ws, wsb = twq._workspace(dev, max(L.twq_quantize_act_workspace_bytes(b, m, r),
                                       L.twq_linear_workspace_bytes(b, m, n, r)))
@@ -170,10 +201,18 @@ def main():
                                 b, m, n, P(ws), wsb, stream), "twq_linear")
 
     def quant(s, stream):
-        twq._check(L.twq_quantize_act(P(s["x"]), b, m, P(s["qx"]), P(s["sx"]), P(s["l1t"]), r, P(s["t"]),
-                                      P(ws), wsb, stream), "twq_quantize_act")
+        twq._check(L.twq_quantize_act(P(s["x"]), b, m, P(s["qx"]), P(s["sx"]), P(s["l1t"]), 0 if lr4 else r,
+                                      P(s["t"]), P(ws), wsb, stream), "twq_quantize_act")
+        if lr4 and r:
+            twq._check(L.twq_lowrank_requant(P(s["qx"]), P(s["sx"]), P(s["ql1"]), P(s["c"]), r, P(s["h"]),
+                                             P(s["qh"]), P(s["sh"]), b, m, stream), "twq_lowrank_requant")
 
     def dual(s, stream):
+        if lr4:
+            twq._check(L.twq_dual_linear_lr4(P(s["qx"]), P(s["sx"]), P(s["qw"]), P(s["sw"]), P(s["qh"]),
+                                             P(s["sh"]), P(s["ql2"]), r, P(s["y"]), b, m, n, stream),
+                       "twq_dual_linear_lr4")
+            return
         twq._check(L.twq_dual_linear(P(s["qx"]), P(s["sx"]), P(s["qw"]), P(s["sw"]), P(s["t"]), P(s["l2t"]), r,
                                      P(s["y"]), b, m, n, stream), "twq_dual_linear")
 
@@ -199,7 +238,7 @@ def main():
                 s = sets[(i + offset) % copies]
                 if not with_quant:
                     dual(s, st)
-                elif args.path == "linear":
+                elif args.path == "linear" and not lr4:
                     layer(s, st)
                 else:
                     quant(s, st)
@@ -252,17 +291,20 @@ def main():
     ops = layer_ops(b, m, n, r)
     tops = ops / (ms_step * 1e-3) / 1e12
     decode = b <= 64
+    kbytes = dual_linear_lr4_bytes(b, m, n, r) if lr4 else dual_linear_bytes(b, m, n, r)
+    cbytes = call_bytes_lr4(b, m, n, r) if lr4 else call_bytes(b, m, n, r)
+    traffic = None if lr4 else measured_traffic(args.config)
     if decode:
-        ach = dual_linear_bytes(b, m, n, r) / (us_dual * 1e-6) / 1e9
+        ach = kbytes / (us_dual * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic(args.config)}
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         ach = 2 * b * m * n / (us_dual * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": measured_traffic(args.config)}
-    roof["kernel"] = "twq_dual_linear"
+                "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": traffic}
+    roof["kernel"] = "twq_dual_linear_lr4" if lr4 else "twq_dual_linear"
     roof["kernel_us"] = round(us_dual, 3)
-    roof["algorithmic_bytes"] = dual_linear_bytes(b, m, n, r)
+    roof["algorithmic_bytes"] = kbytes
     roof["algorithmic_int8_ops"] = 2 * b * m * n
 
     out = {
@@ -277,19 +319,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes on i8 MFMA (int32 acc) + fp16 low-rank (fp32 acc)",
+        "dtype": ("int4 codes on i8 MFMA (int32 acc), int4 low-rank on i8 MFMA" if lr4 else
+                  "int4 codes on i8 MFMA (int32 acc) + fp16 low-rank (fp32 acc)"),
         "data": "synthetic",
         "config": {"workload": f"{args.config}: b={b} m={m} n={n} r={r}", "b": b, "m": m, "n": n, "r": r,
                    "weight_copies_rotated": copies, "launch": "eager" if args.eager else "hip_graph",
-                   "entry_points": "twq_linear" if args.path == "linear" else "twq_quantize_act+twq_dual_linear",
-                   "call_bytes": call_bytes(b, m, n, r),
-                   "hbm_frac_whole_call": round(call_bytes(b, m, n, r) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                   "lowrank": args.lowrank,
+                   "entry_points": ("twq_quantize_act+twq_lowrank_requant+twq_dual_linear_lr4" if lr4 else
+                                    "twq_linear" if args.path == "linear" else "twq_quantize_act+twq_dual_linear"),
+                   "call_bytes": cbytes,
+                   "hbm_frac_whole_call": round(cbytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                    "int8_mfma_frac_whole_call": round(2 * b * m * n / (ms_step * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)},
         "roofline": roof,
     }
     if not args.no_cpu:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = _cpu_baseline(d)
+        out["cpu_baseline"] = _cpu_baseline(d, lr4=lr4)
         out["cpu_baseline"]["host"] = platform.processor() or platform.machine()
     print(json.dumps(out), flush=True)
 
