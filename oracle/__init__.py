@@ -61,6 +61,13 @@ def _load():
         lib.orc_dual_linear_lr4.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P]
         lib.orc_dual_linear_lr4_sampled.restype = ctypes.c_int
         lib.orc_dual_linear_lr4_sampled.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P]
+        lib.orc_quantize_act_grouped.argtypes = [_P, _I, _I, _I, _P, _P, _P]
+        lib.orc_quantize_weight_grouped.argtypes = [_P, _I, _I, _I, _P, _P, _P]
+        lib.orc_residual_acc_grouped.argtypes = [_P, _P, _I, _I, _I, _I, _P]
+        lib.orc_dual_linear_grouped.restype = ctypes.c_int
+        lib.orc_dual_linear_grouped.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
+        lib.orc_dual_linear_grouped_sampled.restype = ctypes.c_int
+        lib.orc_dual_linear_grouped_sampled.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P]
         lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -262,6 +269,90 @@ def dual_linear_lr4_sampled(x, w_res, l1t, l2t, rows, cols):
     if rc:
         raise MemoryError("oracle allocation failed")
     return acc, acc2, y
+
+
+def _check_group(m, g):
+    if g <= 0 or g % 2 or m % g:
+        raise ValueError(f"group size {g} must be even and divide m = {m}")
+
+
+def quantize_act_grouped(x, g):
+    """Group-wise activation quantizer: (codes int8 [b][m], packed u8 [b][m/2], s_X f32 [b][m/g])."""
+    xb = _h(x)
+    b, m = xb.shape
+    _check_group(m, g)
+    q = np.empty((b, m), np.int8)
+    qp = np.empty((b, m // 2), np.uint8)
+    s = np.empty((b, m // g), np.float32)
+    _load().orc_quantize_act_grouped(_p(xb), b, m, g, _p(q), _p(qp), _p(s))
+    return q, qp, s
+
+
+def quantize_weight_grouped(w, g):
+    """Group-wise weight quantizer: (codes int8 [n][m], packed u8 [n][m/2], s_W f32 [n][m/g])."""
+    w = _c(w, np.float32)
+    n, m = w.shape
+    _check_group(m, g)
+    q = np.empty((n, m), np.int8)
+    qp = np.empty((n, m // 2), np.uint8)
+    s = np.empty((n, m // g), np.float32)
+    _load().orc_quantize_weight_grouped(_p(w), n, m, g, _p(q), _p(qp), _p(s))
+    return q, qp, s
+
+
+def residual_acc_grouped(qx, qw, g):
+    """int64 [b][n][m/g]: the integer sum of each group of K separately."""
+    qx = _c(qx, np.int8)
+    qw = _c(qw, np.int8)
+    b, m = qx.shape
+    n = qw.shape[0]
+    _check_group(m, g)
+    acc = np.empty((b, n, m // g), np.int64)
+    _load().orc_residual_acc_grouped(_p(qx), _p(qw), b, m, n, g, _p(acc))
+    return acc
+
+
+def dual_linear_grouped(x, w_res, l1t, l2t, g):
+    """The layer with group-wise scales: dict qx_packed, sx [b][m/g], qw_packed, sw [n][m/g], y."""
+    xb = _h(x)
+    w = _c(w_res, np.float32)
+    b, m = xb.shape
+    n = w.shape[0]
+    _check_group(m, g)
+    l1 = _h(l1t) if l1t is not None else np.zeros((0, m), np.uint16)
+    l2 = _h(l2t) if l2t is not None else np.zeros((n, 0), np.uint16)
+    r = l1.shape[0]
+    out = {"qx_packed": np.empty((b, m // 2), np.uint8), "sx": np.empty((b, m // g), np.float32),
+           "qw_packed": np.empty((n, m // 2), np.uint8), "sw": np.empty((n, m // g), np.float32),
+           "y": np.empty((b, n), np.float64)}
+    rc = _load().orc_dual_linear_grouped(_p(xb), _p(w), _p(l1), _p(l2), b, m, n, r, g,
+                                         _p(out["qx_packed"]), _p(out["sx"]), _p(out["qw_packed"]),
+                                         _p(out["sw"]), _p(out["y"]))
+    if rc:
+        raise MemoryError("oracle allocation failed")
+    return out
+
+
+def dual_linear_grouped_sampled(x, w_res, l1t, l2t, g, rows, cols):
+    """Y of the group-wise layer at the positions (rows[p], cols[p])."""
+    xb = _h(x)
+    w = _c(w_res, np.float32)
+    b, m = xb.shape
+    n = w.shape[0]
+    _check_group(m, g)
+    l1 = _h(l1t) if l1t is not None else np.zeros((0, m), np.uint16)
+    l2 = _h(l2t) if l2t is not None else np.zeros((n, 0), np.uint16)
+    r = l1.shape[0]
+    rows = _c(rows, np.int64)
+    cols = _c(cols, np.int64)
+    assert rows.shape == cols.shape and rows.ndim == 1
+    assert ((0 <= rows) & (rows < b)).all() and ((0 <= cols) & (cols < n)).all()
+    y = np.empty(rows.shape[0], np.float64)
+    rc = _load().orc_dual_linear_grouped_sampled(_p(xb), _p(w), _p(l1), _p(l2), b, m, n, r, g, _p(rows),
+                                                 _p(cols), rows.shape[0], _p(y))
+    if rc:
+        raise MemoryError("oracle allocation failed")
+    return y
 
 
 def unpack_codes(packed):

@@ -34,7 +34,10 @@
  * force of the integer GEMM, the identities r = 0 (plain W4A4, a library int64
  * matmul) and W_res = 0 (pure low-rank, a library fp64 matmul), a hand-worked
  * whole layer, and for the int4 low-rank variant a hand-worked case plus the
- * identity that exactly representable factors reproduce the fp16 branch.
+ * identity that exactly representable factors reproduce the fp16 branch; for
+ * group-wise scales a hand-worked two-group layer, the identities g = m (one
+ * group: the per-token layer) and grouped rows = per-row quantization of the
+ * rows cut into groups, and brute force with exact rationals.
  * The pages' own kernel numerics (its s_H granularity in particular) print no
  * example and stay a reading, not a pin.
  */
@@ -429,4 +432,155 @@ int orc_max_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* ---- group-wise scales (TwinQuant page 1, section 5.1, and page 2, section 5.1:
+ * weights and activations are quantized group-wise, groups of 128) ----
+ *
+ * Reading: a group is a run of g consecutive elements along the reduction
+ * dimension K of one token row of X or one output channel of W_res; eq. (1)
+ * applies to each group on its own, with its own binary32 scale. The integer
+ * sum of eq. (2) then splits into one sum per group, each carrying the product
+ * of its two group scales:
+ *
+ *   Y[i][j] = sum_G s_X[i][G] s_W[j][G] acc_G[i][j] + LR[i][j],
+ *   acc_G[i][j] = sum_{k in G} Q_X[i][k] Q_W[j][k].
+ *
+ * Scales are stored row by row: s_X [b][m/g], s_W [n][m/g]. */
+
+/* X fp16 [b][m] -> codes int8 [b][m], packed u8 [b][m/2] (may be NULL), s_X f32 [b][m/g] */
+void orc_quantize_act_grouped(const uint16_t *x, int64_t b, int64_t m, int64_t g, int8_t *qx,
+                              uint8_t *qx_packed, float *sx)
+{
+    const int64_t ng = m / g;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < b; i++) {
+        float *row = (float *)malloc(sizeof(float) * (size_t)m);
+        for (int64_t k = 0; k < m; k++)
+            row[k] = (float)orc_half_to_double(x[i * m + k]);
+        for (int64_t G = 0; G < ng; G++)
+            quantize_vector(row + G * g, g, qx + i * m + G * g, sx + i * ng + G);
+        if (qx_packed)
+            pack_codes(qx + i * m, m, qx_packed + i * (m / 2));
+        free(row);
+    }
+}
+
+/* W_res f32 [n][m] -> codes int8 [n][m], packed u8 [n][m/2] (may be NULL), s_W f32 [n][m/g] */
+void orc_quantize_weight_grouped(const float *w, int64_t n, int64_t m, int64_t g, int8_t *qw,
+                                 uint8_t *qw_packed, float *sw)
+{
+    const int64_t ng = m / g;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; j++) {
+        for (int64_t G = 0; G < ng; G++)
+            quantize_vector(w + j * m + G * g, g, qw + j * m + G * g, sw + j * ng + G);
+        if (qw_packed)
+            pack_codes(qw + j * m, m, qw_packed + j * (m / 2));
+    }
+}
+
+/* acc_G[i][j][G] = sum over k in group G of Q_X[i][k] Q_W[j][k], int64, layout [b][n][m/g] */
+void orc_residual_acc_grouped(const int8_t *qx, const int8_t *qw, int64_t b, int64_t m, int64_t n,
+                              int64_t g, int64_t *acc)
+{
+    const int64_t ng = m / g;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < b; i++)
+        for (int64_t j = 0; j < n; j++)
+            for (int64_t G = 0; G < ng; G++) {
+                int64_t sum = 0;
+                for (int64_t k = G * g; k < (G + 1) * g; k++)
+                    sum += (int64_t)qx[i * m + k] * (int64_t)qw[j * m + k];
+                acc[(i * n + j) * ng + G] = sum;
+            }
+}
+
+/* The whole layer with group-wise scales and the fp16 low-rank branch, binary64:
+ * Y[i][j] = sum_G s_X[i][G] s_W[j][G] acc_G[i][j] + LR[i][j].
+ * Outputs other than y may be NULL. */
+int orc_dual_linear_grouped(const uint16_t *x, const float *w_res, const uint16_t *l1t,
+                            const uint16_t *l2t, int64_t b, int64_t m, int64_t n, int64_t r,
+                            int64_t g, uint8_t *qx_packed, float *sx, uint8_t *qw_packed,
+                            float *sw, double *y)
+{
+    const int64_t ng = m / g;
+    int8_t *qx = (int8_t *)malloc((size_t)(b * m));
+    int8_t *qw = (int8_t *)malloc((size_t)(n * m));
+    float *sx_l = (float *)malloc(sizeof(float) * (size_t)(b * ng));
+    float *sw_l = (float *)malloc(sizeof(float) * (size_t)(n * ng));
+    int64_t *acc = (int64_t *)malloc(sizeof(int64_t) * (size_t)(b * n * ng));
+    double *t = (double *)malloc(sizeof(double) * (size_t)(b * (r > 0 ? r : 1)));
+    double *lr = (double *)malloc(sizeof(double) * (size_t)(b * n));
+    if (!qx || !qw || !sx_l || !sw_l || !acc || !t || !lr)
+        return 1;
+    orc_quantize_act_grouped(x, b, m, g, qx, qx_packed, sx_l);
+    orc_quantize_weight_grouped(w_res, n, m, g, qw, qw_packed, sw_l);
+    orc_residual_acc_grouped(qx, qw, b, m, n, g, acc);
+    if (r > 0) {
+        orc_lowrank_t(x, l1t, b, m, r, t);
+        orc_lowrank_out(t, l2t, b, n, r, lr);
+    } else {
+        memset(lr, 0, sizeof(double) * (size_t)(b * n));
+    }
+    for (int64_t i = 0; i < b; i++)
+        for (int64_t j = 0; j < n; j++) {
+            double sum = 0.0;
+            for (int64_t G = 0; G < ng; G++)
+                sum += (double)sx_l[i * ng + G] * (double)sw_l[j * ng + G] *
+                       (double)acc[(i * n + j) * ng + G];
+            y[i * n + j] = sum + lr[i * n + j];
+        }
+    if (sx)
+        memcpy(sx, sx_l, sizeof(float) * (size_t)(b * ng));
+    if (sw)
+        memcpy(sw, sw_l, sizeof(float) * (size_t)(n * ng));
+    free(qx); free(qw); free(sx_l); free(sw_l); free(acc); free(t); free(lr);
+    return 0;
+}
+
+/* Y of the group-wise layer at sampled positions only: Y[rows[p]][cols[p]]. */
+int orc_dual_linear_grouped_sampled(const uint16_t *x, const float *w_res, const uint16_t *l1t,
+                                    const uint16_t *l2t, int64_t b, int64_t m, int64_t n,
+                                    int64_t r, int64_t g, const int64_t *rows,
+                                    const int64_t *cols, int64_t count, double *y_out)
+{
+    (void)b;
+    (void)n;
+    const int64_t ng = m / g;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < count; p++) {
+        int64_t i = rows[p], j = cols[p];
+        float *xr = (float *)malloc(sizeof(float) * (size_t)m);
+        int8_t *qx = (int8_t *)malloc((size_t)m);
+        int8_t *qw = (int8_t *)malloc((size_t)m);
+        float *sxi = (float *)malloc(sizeof(float) * (size_t)ng);
+        float *swj = (float *)malloc(sizeof(float) * (size_t)ng);
+        if (!xr || !qx || !qw || !sxi || !swj) {
+            fail = 1;
+            continue;
+        }
+        for (int64_t k = 0; k < m; k++)
+            xr[k] = (float)orc_half_to_double(x[i * m + k]);
+        double y = 0.0;
+        for (int64_t G = 0; G < ng; G++) {
+            quantize_vector(xr + G * g, g, qx + G * g, sxi + G);
+            quantize_vector(w_res + j * m + G * g, g, qw + G * g, swj + G);
+            int64_t acc = 0;
+            for (int64_t k = G * g; k < (G + 1) * g; k++)
+                acc += (int64_t)qx[k] * (int64_t)qw[k];
+            y += (double)sxi[G] * (double)swj[G] * (double)acc;
+        }
+        double lr = 0.0;
+        for (int64_t u = 0; u < r; u++) {
+            double tu = 0.0;
+            for (int64_t k = 0; k < m; k++)
+                tu += orc_half_to_double(x[i * m + k]) * orc_half_to_double(l1t[u * m + k]);
+            lr += tu * orc_half_to_double(l2t[j * r + u]);
+        }
+        y_out[p] = y + lr;
+        free(xr); free(qx); free(qw); free(sxi); free(swj);
+    }
+    return fail;
 }

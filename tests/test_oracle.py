@@ -386,3 +386,123 @@ def test_generators_deterministic_and_outliers():
     # the 4 outlier channels of the tiny config dominate the column maxima
     colmax = np.abs(a["x"].astype(np.float64)).max(axis=0)
     assert (np.sort(colmax)[-4:] > 10 * np.median(colmax)).all()
+
+
+# ---------------------------------------------------------------- group-wise scales (g = 128 in the pages' experiments)
+
+def _grouped():
+    with open(os.path.join(GOLDEN, "grouped_layer.json")) as f:
+        return json.load(f)
+
+
+def test_grouped_hand_worked(oracle_lib):
+    gd = _grouped()
+    g = gd["g"]
+    x = np.array(gd["x"], np.float16)
+    w = np.array(gd["w_res"], np.float32)
+    qx, qxp, sx = oracle_lib.quantize_act_grouped(x, g)
+    qw, qwp, sw = oracle_lib.quantize_weight_grouped(w, g)
+    assert qx.tolist() == gd["qx"] and qxp.tolist() == gd["qx_packed"]
+    assert qw.tolist() == gd["qw"] and qwp.tolist() == gd["qw_packed"]
+    assert sx.astype(np.float64).tolist() == gd["sx"] and sw.astype(np.float64).tolist() == gd["sw"]
+    assert oracle_lib.residual_acc_grouped(qx, qw, g).tolist() == gd["acc_grouped"]
+    out = oracle_lib.dual_linear_grouped(x, w, None, None, g)
+    assert out["y"].tolist() == gd["y"]
+    assert out["qx_packed"].tolist() == gd["qx_packed"] and out["sw"].astype(np.float64).tolist() == gd["sw"]
+    # one scale per token gives different codes for the first group
+    assert oracle_lib.quantize_act(x)[0][0].tolist() == gd["qx_per_token_row0"]
+
+
+def test_grouped_rational_bruteforce(oracle_lib):
+    """Codes, scales and Y of the group-wise layer from exact rationals (binary32 roundings
+    decided by the rational model), including the low-rank branch."""
+    rng = synth.rng_for(40)
+    b, m, n, r, g = 3, 16, 5, 2, 4
+    x = (rng.standard_normal((b, m)) * np.array([1, 1, 1, 30] * 4)).astype(np.float16)
+    x[1, 4:8] = 0  # an all-zero group
+    w = (rng.standard_t(3, size=(n, m)) * 0.02).astype(np.float32)
+    w[2, 8:12] = 0
+    l1t = rng.standard_normal((r, m)).astype(np.float16)
+    l2t = rng.standard_normal((n, r)).astype(np.float16)
+    out = oracle_lib.dual_linear_grouped(x, w, l1t, l2t, g)
+    qx = oracle_lib.unpack_codes(out["qx_packed"])
+    qw = oracle_lib.unpack_codes(out["qw_packed"])
+    xf = [[F(float(v)) for v in row] for row in x]
+    wf = [[F(float(v)) for v in row] for row in w]
+    for i in range(b):
+        for G in range(m // g):
+            s, q = ratmodel.quantize(xf[i][G * g:(G + 1) * g])
+            assert F(float(out["sx"][i, G])) == s and qx[i, G * g:(G + 1) * g].tolist() == q
+    for j in range(n):
+        for G in range(m // g):
+            s, q = ratmodel.quantize(wf[j][G * g:(G + 1) * g])
+            assert F(float(out["sw"][j, G])) == s and qw[j, G * g:(G + 1) * g].tolist() == q
+    l1 = [[F(float(v)) for v in row] for row in l1t]
+    l2 = [[F(float(v)) for v in row] for row in l2t]
+    for i in range(b):
+        t = [sum(xf[i][k] * l1[u][k] for k in range(m)) for u in range(r)]
+        for j in range(n):
+            y = sum(F(float(out["sx"][i, G])) * F(float(out["sw"][j, G])) *
+                    sum(int(qx[i, k]) * int(qw[j, k]) for k in range(G * g, (G + 1) * g))
+                    for G in range(m // g))
+            y += sum(t[u] * l2[j][u] for u in range(r))
+            assert abs(float(y) - out["y"][i, j]) <= 1e-12 * max(1.0, abs(float(y)))
+
+
+def test_grouped_one_group_is_per_token(oracle_lib):
+    """g = m: one group per row, which is the per-token / per-channel layer exactly."""
+    d = synth.make_random(6, 96, 20, 16, seed=41)
+    m = d["x"].shape[1]
+    gl = oracle_lib.dual_linear_grouped(d["x"], d["w_res"], d["l1t"], d["l2t"], m)
+    pl = oracle_lib.dual_linear(d["x"], d["w_res"], d["l1t"], d["l2t"])
+    assert (gl["qx_packed"] == pl["qx_packed"]).all() and (gl["qw_packed"] == pl["qw_packed"]).all()
+    assert (gl["sx"][:, 0] == pl["sx"]).all() and (gl["sw"][:, 0] == pl["sw"]).all()
+    assert (gl["y"] == pl["y"]).all()
+
+
+def test_grouped_rows_are_per_row_quantization(oracle_lib):
+    """Each group is eq. (1) on its own: the group-wise quantizer of a [rows][m] matrix is the
+    per-row quantizer of the same matrix cut into [rows m / g][g]."""
+    d = synth.make_random(4, 512, 24, 16, seed=42)
+    for g in (128, 32, 512):
+        qx, _, sx = oracle_lib.quantize_act_grouped(d["x"], g)
+        qx1, _, sx1 = oracle_lib.quantize_act(d["x"].reshape(-1, g))
+        assert (qx.reshape(-1, g) == qx1).all() and (sx.reshape(-1) == sx1).all()
+        qw, _, sw = oracle_lib.quantize_weight_grouped(d["w_res"], g)
+        qw1, _, sw1 = oracle_lib.quantize_weight(d["w_res"].reshape(-1, g))
+        assert (qw.reshape(-1, g) == qw1).all() and (sw.reshape(-1) == sw1).all()
+
+
+def test_grouped_scales_are_local(oracle_lib):
+    """An outlier changes the codes and scale of its own group and nothing else."""
+    rng = synth.rng_for(43)
+    x = rng.standard_normal((2, 512)).astype(np.float16)
+    q0, _, s0 = oracle_lib.quantize_act_grouped(x, 128)
+    x2 = x.copy()
+    x2[0, 300] = 900.0  # group 2 of row 0
+    q1, _, s1 = oracle_lib.quantize_act_grouped(x2, 128)
+    changed = s1 != s0
+    assert changed.tolist() == [[False, False, True, False], [False, False, False, False]]
+    keep = np.ones((2, 512), bool)
+    keep[0, 256:384] = False
+    assert (q0[keep] == q1[keep]).all() and (q0[0, 256:384] != q1[0, 256:384]).any()
+
+
+def test_grouped_acc_sums_to_whole_acc(oracle_lib):
+    rng = synth.rng_for(44)
+    qx = rng.integers(-7, 8, size=(5, 256)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(7, 256)).astype(np.int8)
+    accg = oracle_lib.residual_acc_grouped(qx, qw, 64)
+    assert (accg.sum(axis=2) == oracle_lib.residual_acc(qx, qw)).all()
+    i, j, G = 3, 5, 2
+    assert accg[i, j, G] == sum(int(qx[i, k]) * int(qw[j, k]) for k in range(128, 192))
+
+
+def test_grouped_sampled_matches_full(oracle_lib):
+    d = synth.make_random(10, 384, 40, 16, seed=45)
+    full = oracle_lib.dual_linear_grouped(d["x"], d["w_res"], d["l1t"], d["l2t"], 128)
+    rng = synth.rng_for(46)
+    rows = rng.integers(0, 10, 50)
+    cols = rng.integers(0, 40, 50)
+    y = oracle_lib.dual_linear_grouped_sampled(d["x"], d["w_res"], d["l1t"], d["l2t"], 128, rows, cols)
+    assert (y == full["y"][rows, cols]).all()
