@@ -152,6 +152,39 @@ twq_status twq_linear(const void *x, const void *qw, const float *sw, const void
                       size_t workspace_bytes, void *stream);
 
 /*
+ * ---- group-wise scales (TwinQuant page 1, section 5.1 and page 2, section 5.1:
+ * weights and activations quantized group-wise, groups of 128) ----
+ *
+ * Reading: a group is g consecutive elements along K (the input dimension) of one
+ * token row of X or one output channel of W_res; eq. (1) quantizes each group with
+ * its own scale, and the integer sum of eq. (2) splits into one sum per group:
+ *
+ *   Y[i][j] = fp16( sum_G s_X[G][i] s_W[G][j] sum_{k in G} Q_X[i][k] Q_W[j][k]
+ *                   + sum_t T[i][t] L2[t][j] )
+ *
+ * Each group's integer sum is exact (int32); the scaled group sums are added in
+ * fp32. The codes use the packed format above. Scales are group-major (one row of
+ * the array per group), the layout the main loops read a group's scales of a whole
+ * tile in one piece from:
+ *   s_X  f32 [m/g][b]    s_X[G][i] of token i, group G (elements G g .. G g + g - 1)
+ *   s_W  f32 [m/g][n]    s_W[G][j] of output channel j, group G
+ * g must be 128 (TWQ_ERR_UNSUPPORTED otherwise). The other arguments, the
+ * workspace rules and the errors are those of the per-token entry points.
+ */
+twq_status twq_quantize_act_grouped(const void *x, int64_t b, int64_t m, int64_t g, void *qx,
+                                    float *sx, const void *l1t, int64_t r, float *t,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+twq_status twq_pack_weight_grouped(const float *w_res, int64_t n, int64_t m, int64_t g, void *qw,
+                                   float *sw, void *stream);
+twq_status twq_dual_linear_grouped(const void *qx, const float *sx, const void *qw, const float *sw,
+                                   const float *t, const void *l2t, int64_t r, void *y, int64_t b,
+                                   int64_t m, int64_t n, int64_t g, void *stream);
+size_t twq_linear_grouped_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r, int64_t g);
+twq_status twq_linear_grouped(const void *x, const void *qw, const float *sw, const void *l1t,
+                              const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n,
+                              int64_t g, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * ---- int4 low-rank variant (TwinQuant page 1, section 4.3) ----
  *
  * Both low-rank factors in 4 bits: the first low-rank GEMM gives INT32 H = Q_X Q_L1,

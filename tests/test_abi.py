@@ -10,7 +10,7 @@ import w4a4_rank_gemm_amd as twq
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "twq.h")
 
-OK, NULL, SHAPE, ALIGN, WORKSPACE = 0, 1, 2, 3, 6
+OK, NULL, SHAPE, ALIGN, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3, 4, 6
 A = ctypes.c_void_p(4096)       # an aligned, never-dereferenced address
 MIS = ctypes.c_void_p(4096 + 8)  # misaligned
 
@@ -125,3 +125,25 @@ def test_linear_validation():
     assert L.twq_linear(A, A, A, A, A, 24, A, 16, 4096, 4096, A, need, None) == SHAPE
     assert L.twq_linear(A, A, A, A, A, 32, A, 16, 4096, 40, A, need, None) == SHAPE
     assert L.twq_linear(None, None, None, None, None, 32, None, 0, 4096, 4096, None, 0, None) == OK
+
+
+def test_grouped_validation():
+    """Group-wise entry points: only g = 128 is supported; the other checks are those of the
+    per-token entry points, and a grouped layer needs room for m/128 scales per token."""
+    L = twq.lib()
+    for g in (64, 256, 0, -128):
+        assert L.twq_quantize_act_grouped(A, 16, 4096, g, A, A, None, 0, None, None, 0, None) == UNSUPPORTED
+        assert L.twq_pack_weight_grouped(A, 64, 4096, g, A, A, None) == UNSUPPORTED
+        assert L.twq_dual_linear_grouped(A, A, A, A, None, None, 0, A, 16, 4096, 64, g, None) == UNSUPPORTED
+        assert L.twq_linear_grouped_workspace_bytes(16, 4096, 64, 0, g) == 0
+    assert L.twq_quantize_act_grouped(A, 16, 4000, 128, A, A, None, 0, None, None, 0, None) == SHAPE
+    assert L.twq_quantize_act_grouped(None, 16, 4096, 128, A, A, None, 0, None, None, 0, None) == NULL
+    assert L.twq_pack_weight_grouped(A, 40, 4096, 128, A, A, None) == SHAPE
+    assert L.twq_pack_weight_grouped(A, 64, 4096, 128, MIS, A, None) == ALIGN
+    assert L.twq_dual_linear_grouped(A, A, A, A, None, None, 32, A, 16, 4096, 64, 128, None) == NULL
+    assert L.twq_dual_linear_grouped(A, A, A, A, None, None, 0, A, 0, 4096, 64, 128, None) == OK
+    per_token = L.twq_linear_workspace_bytes(16, 4096, 4096, 32)
+    grouped = L.twq_linear_grouped_workspace_bytes(16, 4096, 4096, 32, 128)
+    assert grouped >= per_token + 16 * 4 * (4096 // 128 - 1) - 255
+    assert L.twq_linear_grouped(A, A, A, A, A, 32, A, 16, 4096, 4096, 128, A, grouped - 1, None) == WORKSPACE
+    assert L.twq_linear_grouped(None, None, None, None, None, 32, None, 0, 4096, 4096, 128, None, 0, None) == OK

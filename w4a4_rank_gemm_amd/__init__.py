@@ -28,7 +28,11 @@ STATUS_NAMES = {0: "TWQ_OK", 1: "TWQ_ERR_NULL", 2: "TWQ_ERR_SHAPE", 3: "TWQ_ERR_
 EXPORTS = ("twq_status_string", "twq_last_error_string", "twq_version",
            "twq_quantize_act_workspace_bytes", "twq_quantize_act", "twq_pack_weight",
            "twq_dual_linear", "twq_debug_residual_acc", "twq_linear_workspace_bytes",
-           "twq_linear", "twq_pack_lowrank_int4", "twq_lowrank_requant", "twq_dual_linear_lr4")
+           "twq_linear", "twq_quantize_act_grouped", "twq_pack_weight_grouped", "twq_dual_linear_grouped",
+           "twq_linear_grouped_workspace_bytes", "twq_linear_grouped", "twq_pack_lowrank_int4",
+           "twq_lowrank_requant", "twq_dual_linear_lr4")
+
+GROUP = 128  # group size of the group-wise entry points
 
 
 class TwqError(RuntimeError):
@@ -74,6 +78,16 @@ def lib() -> ctypes.CDLL:
                 L.twq_linear_workspace_bytes.argtypes = [_I, _I, _I, _I]
                 L.twq_linear.restype = ctypes.c_int
                 L.twq_linear.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _S, _P]
+                L.twq_quantize_act_grouped.restype = ctypes.c_int
+                L.twq_quantize_act_grouped.argtypes = [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _S, _P]
+                L.twq_pack_weight_grouped.restype = ctypes.c_int
+                L.twq_pack_weight_grouped.argtypes = [_P, _I, _I, _I, _P, _P, _P]
+                L.twq_dual_linear_grouped.restype = ctypes.c_int
+                L.twq_dual_linear_grouped.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _P]
+                L.twq_linear_grouped_workspace_bytes.restype = _S
+                L.twq_linear_grouped_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+                L.twq_linear_grouped.restype = ctypes.c_int
+                L.twq_linear_grouped.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _P, _S, _P]
                 L.twq_pack_lowrank_int4.restype = ctypes.c_int
                 L.twq_pack_lowrank_int4.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]
                 L.twq_lowrank_requant.restype = ctypes.c_int
@@ -220,6 +234,97 @@ def linear(x: torch.Tensor, qw, sw, l1t=None, l2t=None, out: torch.Tensor | None
     ws, wsb = _workspace(dev, L.twq_linear_workspace_bytes(b, m, n, r))
     _check(L.twq_linear(_ptr(x), _ptr(qw), _ptr(sw), _ptr(l1t), _ptr(l2t), r, _ptr(y), b, m, n,
                         _ptr(ws), wsb, _stream(dev)), "twq_linear")
+    return y
+
+
+# ---- group-wise scales (groups of GROUP along K; scales group-major) ----
+
+def quantize_act_grouped(x: torch.Tensor, l1t: torch.Tensor | None = None, g: int = GROUP):
+    """X fp16 [b][m] -> (Q_X u8 [b][m/2], s_X f32 [m/g][b], T f32 [b][r] or None)."""
+    _need(x, "x", torch.float16, 2)
+    b, m = x.shape
+    r = 0
+    if l1t is not None:
+        _need(l1t, "l1t", torch.float16, 2)
+        r = l1t.shape[0]
+        if l1t.shape[1] != m or l1t.device != x.device:
+            raise ValueError("l1t must be [r][m] on x's device")
+    dev = x.device
+    qx = torch.empty((b, m // 2), dtype=torch.uint8, device=dev)
+    sx = torch.empty((m // g, b), dtype=torch.float32, device=dev)
+    t = torch.empty((b, r), dtype=torch.float32, device=dev) if r else None
+    L = lib()
+    ws, wsb = _workspace(dev, L.twq_quantize_act_workspace_bytes(b, m, r))
+    _check(L.twq_quantize_act_grouped(_ptr(x), b, m, g, _ptr(qx), _ptr(sx), _ptr(l1t), r, _ptr(t),
+                                      _ptr(ws), wsb, _stream(dev)), "twq_quantize_act_grouped")
+    return qx, sx, t
+
+
+def pack_weight_grouped(w_res: torch.Tensor, g: int = GROUP):
+    """W_res f32 [n][m] -> (Q_W u8 [n][m/2], s_W f32 [m/g][n])."""
+    _need(w_res, "w_res", torch.float32, 2)
+    n, m = w_res.shape
+    dev = w_res.device
+    qw = torch.empty((n, m // 2), dtype=torch.uint8, device=dev)
+    sw = torch.empty((m // g, n), dtype=torch.float32, device=dev)
+    _check(lib().twq_pack_weight_grouped(_ptr(w_res), n, m, g, _ptr(qw), _ptr(sw), _stream(dev)),
+           "twq_pack_weight_grouped")
+    return qw, sw
+
+
+def dual_linear_grouped(qx, sx, qw, sw, t=None, l2t=None, out: torch.Tensor | None = None, g: int = GROUP):
+    """The fused layer with group-wise scales: Y fp16 [b][n]."""
+    _need(qx, "qx", torch.uint8, 2)
+    _need(qw, "qw", torch.uint8, 2)
+    _need(sx, "sx", torch.float32, 2)
+    _need(sw, "sw", torch.float32, 2)
+    b, kb = qx.shape
+    n = qw.shape[0]
+    m = 2 * kb
+    if qw.shape[1] != kb or sx.shape != (m // g, b) or sw.shape != (m // g, n):
+        raise ValueError("inconsistent shapes of qx/sx/qw/sw")
+    r = 0
+    if l2t is not None or t is not None:
+        _need(t, "t", torch.float32, 2)
+        _need(l2t, "l2t", torch.float16, 2)
+        r = l2t.shape[1]
+        if t.shape != (b, r) or l2t.shape[0] != n:
+            raise ValueError("t must be [b][r] and l2t [n][r]")
+    dev = qx.device
+    y = out if out is not None else torch.empty((b, n), dtype=torch.float16, device=dev)
+    _need(y, "out", torch.float16, 2)
+    if y.shape != (b, n):
+        raise ValueError("out must be [b][n]")
+    _check(lib().twq_dual_linear_grouped(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(t), _ptr(l2t), r,
+                                         _ptr(y), b, m, n, g, _stream(dev)), "twq_dual_linear_grouped")
+    return y
+
+
+def linear_grouped(x: torch.Tensor, qw, sw, l1t=None, l2t=None, out: torch.Tensor | None = None, g: int = GROUP):
+    """The whole group-wise layer in one call (twq_linear_grouped): Y fp16 [b][n]."""
+    _need(x, "x", torch.float16, 2)
+    _need(qw, "qw", torch.uint8, 2)
+    _need(sw, "sw", torch.float32, 2)
+    b, m = x.shape
+    n = qw.shape[0]
+    if qw.shape[1] != m // 2 or sw.shape != (m // g, n):
+        raise ValueError("inconsistent shapes of x/qw/sw")
+    r = 0
+    if l1t is not None or l2t is not None:
+        _need(l1t, "l1t", torch.float16, 2)
+        _need(l2t, "l2t", torch.float16, 2)
+        r = l1t.shape[0]
+        if l1t.shape[1] != m or l2t.shape != (n, r):
+            raise ValueError("l1t must be [r][m] and l2t [n][r]")
+    dev = x.device
+    y = out if out is not None else torch.empty((b, n), dtype=torch.float16, device=dev)
+    _need(y, "out", torch.float16, 2)
+    if y.shape != (b, n):
+        raise ValueError("out must be [b][n]")
+    L = lib()
+    ws, wsb = _workspace(dev, L.twq_linear_grouped_workspace_bytes(b, m, n, r, g))
+    _check(L.twq_linear_grouped(_ptr(x), _ptr(qw), _ptr(sw), _ptr(l1t), _ptr(l2t), r, _ptr(y), b, m, n, g,
+                                _ptr(ws), wsb, _stream(dev)), "twq_linear_grouped")
     return y
 
 

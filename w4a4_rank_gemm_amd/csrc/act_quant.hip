@@ -95,6 +95,31 @@ __device__ void quantize_row(const ActArgs &a, int64_t i, int sl, int nsl, uint3
     }
 }
 
+// Group-wise scales (groups of kGroup = 128 along K, TwinQuant page 1, section 5.1):
+// slice sl (of nsl) of one token row, in whole groups. Each thread takes one 8-element
+// chunk at a time; a group is 16 chunks on 16 consecutive lanes, so its amax is a
+// 16-lane reduction, and its scale goes to sx[group][row] (group-major).
+__device__ void quantize_row_grouped(const ActArgs &a, int64_t i, int sl, int nsl) {
+    static_assert(kGroup == 128, "a group is 16 chunks of 8");
+    const int64_t ng = a.m / kGroup;
+    const int64_t c_lo = 16 * (ng * sl / nsl), c_hi = 16 * (ng * (sl + 1) / nsl);
+    const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + i * a.m);
+    uint32_t *qr = reinterpret_cast<uint32_t *>(a.qx + i * (a.m / 2));
+    for (int64_t c = c_lo + threadIdx.x; c < c_hi; c += kActThreads) {  // whole 16-lane groups enter together
+        const uint4 v = xr[c];
+        uint32_t mx = absmax8_bits(v, 0u);
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)mx, off, kWave);
+            mx = mx > o ? mx : o;
+        }
+        const float amax = half_bits_to_float(mx);
+        const float s = amax / kQMax;  // correctly rounded binary32 division
+        if ((threadIdx.x & 15) == 0) a.sx[(c / 16) * a.b + i] = s;
+        qr[c] = amax == 0.0f ? 0u : quant8(v, s, 1.0f / s);
+    }
+}
+
 // T tile for many tokens: tokens [128 tm, 128 tm + 128) x all r = 16 NR ranks over K
 // slice ks, in steps of 32 (64 bytes of fp16 per row). The step's 128 X rows and its
 // L1^T rows (NR blocks of 16, padded to a multiple of four blocks with clamped rows)
@@ -270,7 +295,10 @@ __global__ __launch_bounds__(kActThreads) void act_kernel(ActArgs a, ActDev p) {
             t_slices<NT>(a, p, (int)bid, lds);
     } else {
         const int64_t q = bid - p.n_t_ctas;
-        quantize_row(a, q / p.nsl, (int)(q % p.nsl), p.nsl, red);
+        if (a.group)
+            quantize_row_grouped(a, q / p.nsl, (int)(q % p.nsl), p.nsl);
+        else
+            quantize_row(a, q / p.nsl, (int)(q % p.nsl), p.nsl, red);
     }
 }
 

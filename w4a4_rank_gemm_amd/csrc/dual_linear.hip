@@ -60,8 +60,13 @@ __device__ __forceinline__ v4i lr4_tile(const DualArgs &a, int64_t ch_row, int64
 // T partial-sum slices the decode epilogue adds itself, per 32-rank step it loads
 constexpr int kMaxTSlices = 16;
 
-template <int FN, int FM, int U, int RS, bool STORE_ACC, int TK = 1, int NW = 4>
+// Group-wise scales (GRP, groups of kGroup = 128 along K): one 64-byte piece of a
+// packed row is one group, so each piece's integer sum is formed from zero and added to
+// an fp32 accumulator times s_X[group][token] s_W[group][channel], loaded beside the
+// piece; the waves' fp32 partial sums are added through LDS in wave order.
+template <int FN, int FM, int U, int RS, bool STORE_ACC, int TK = 1, int NW = 4, bool GRP = false>
 __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
+    static_assert(!(GRP && STORE_ACC), "group-wise sums are stored dequantized only");
     __shared__ v4i red[NW][FN * FM][kWave];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int li = lane & 15, g = lane >> 4;
@@ -120,7 +125,31 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = v4i{0, 0, 0, 0};
 
-    auto mma = [&](const uint4 (&bw)[FN], const uint4 (&bx)[FM]) {
+    // GRP: fp32 sums over groups; this lane's s_W (channels 4g..4g+3 of each channel
+    // tile) and s_X (token li of each token tile) columns of the group-major scales
+    v4f yg[GRP ? FN : 1][GRP ? FM : 1];
+    const float *swp[GRP ? FN : 1];
+    const float *sxp[GRP ? FM : 1];
+    if constexpr (GRP) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int64_t ch = ch0 + fn * 16 + 4 * g;
+            swp[fn] = a.sw + (ch < a.n ? ch : a.n - 4);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) yg[fn][fm] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int64_t tok = fm * 16 + li;
+            sxp[fm] = a.sx + (tok < a.b ? tok : a.b - 1);
+        }
+    }
+
+    // one 64-byte piece (128 codes, one group) of every operand row; sw4/sx1: that
+    // group's scales (GRP only; s_X pre-multiplied by 2^-8, undoing the x16 x16 of the
+    // expanded operands exactly)
+    auto mma = [&](const uint4 (&bw)[FN], const uint4 (&bx)[FM], const float4 (&sw4)[GRP ? FN : 1],
+                   const float (&sx1)[GRP ? FM : 1]) {
         v4i alo[FN], ahi[FN], blo[FM], bhi[FM];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) unpack16(bw[fn], alo[fn], ahi[fn]);
@@ -130,55 +159,92 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
         for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
-                acc[fn][fm] = mfma_i8(alo[fn], blo[fm], acc[fn][fm]);
-                acc[fn][fm] = mfma_i8(ahi[fn], bhi[fm], acc[fn][fm]);
+                if constexpr (GRP) {
+                    v4i p = mfma_i8(alo[fn], blo[fm], v4i{0, 0, 0, 0});
+                    p = mfma_i8(ahi[fn], bhi[fm], p);
+                    const float swv[4] = {sw4[fn].x, sw4[fn].y, sw4[fn].z, sw4[fn].w};
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) yg[fn][fm][v] += (float)p[v] * (sx1[fm] * swv[v]);
+                } else {
+                    acc[fn][fm] = mfma_i8(alo[fn], blo[fm], acc[fn][fm]);
+                    acc[fn][fm] = mfma_i8(ahi[fn], bhi[fm], acc[fn][fm]);
+                }
             }
+    };
+    auto load_scales = [&](int64_t c, float4 (&sw4)[GRP ? FN : 1], float (&sx1)[GRP ? FM : 1]) {
+        if constexpr (GRP) {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) sw4[fn] = *reinterpret_cast<const float4 *>(swp[fn] + c * a.n);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) sx1[fm] = sxp[fm][c * a.b] * 0x1p-8f;
+        }
     };
     int64_t c = cb;
     for (; c + U <= ce; c += U) {
         uint4 bw[U][FN], bx[U][FM];
+        float4 sw4[U][GRP ? FN : 1];
+        float sx1[U][GRP ? FM : 1];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) bw[u][fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (c + u) * 64);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) bx[u][fm] = *reinterpret_cast<const uint4 *>(xrow[fm] + (c + u) * 64);
+            load_scales(c + u, sw4[u], sx1[u]);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of its first use
 #pragma unroll
-        for (int u = 0; u < U; ++u) mma(bw[u], bx[u]);
+        for (int u = 0; u < U; ++u) mma(bw[u], bx[u], sw4[u], sx1[u]);
     }
     for (; c < ce; ++c) {
         uint4 bw[FN], bx[FM];
+        float4 sw4[GRP ? FN : 1];
+        float sx1[GRP ? FM : 1];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) bw[fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + c * 64);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) bx[fm] = *reinterpret_cast<const uint4 *>(xrow[fm] + c * 64);
-        mma(bw, bx);
+        load_scales(c, sw4, sx1);
+        mma(bw, bx, sw4, sx1);
     }
 
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) red[wave][fn * FM + fm][lane] = acc[fn][fm];
+        for (int fm = 0; fm < FM; ++fm) {
+            if constexpr (GRP)
+                red[wave][fn * FM + fm][lane] = __builtin_bit_cast(v4i, yg[fn][fm]);
+            else
+                red[wave][fn * FM + fm][lane] = acc[fn][fm];
+        }
     __syncthreads();
     for (int tile = wave; tile < TILES; tile += NW) {
         const int fn_e = tile / FM, fm_e = tile % FM;
         v4i sum = red[0][tile][lane];
+        v4f ysum = __builtin_bit_cast(v4f, red[0][tile][lane]);
 #pragma unroll
-        for (int w = 1; w < NW; ++w) sum += red[w][tile][lane];
+        for (int w = 1; w < NW; ++w) {
+            if constexpr (GRP)
+                ysum += __builtin_bit_cast(v4f, red[w][tile][lane]);
+            else
+                sum += red[w][tile][lane];
+        }
         const int64_t ch = ch0 + fn_e * 16 + 4 * g;
         const int64_t tok = fm_e * 16 + li;
         const bool store = ch < a.n && tok < a.b;
         if constexpr (STORE_ACC) {
             if (store) *reinterpret_cast<v4i *>(a.acc + tok * a.n + ch) = sum >> 8;
         } else {
-            const float sxv = a.sx[tok < a.b ? tok : a.b - 1];
-            const float4 sw4 = *reinterpret_cast<const float4 *>(a.sw + (ch < a.n ? ch : a.n - 4));
-            const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
             v4f y;
+            if constexpr (GRP) {
+                y = ysum;
+            } else {
+                const float sxv = a.sx[tok < a.b ? tok : a.b - 1];
+                const float4 sw4 = *reinterpret_cast<const float4 *>(a.sw + (ch < a.n ? ch : a.n - 4));
+                const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
 #pragma unroll
-            for (int v = 0; v < 4; ++v) y[v] = (sxv * swv[v]) * (float)(sum[v] >> 8);
+                for (int v = 0; v < 4; ++v) y[v] = (sxv * swv[v]) * (float)(sum[v] >> 8);
+            }
             if (a.lr4) {
                 if (a.r > 0) {
                     const v4i acc2 = lr4_tile(a, ch0 + fn_e * 16 + li, fm_e * 16 + li, g);
@@ -225,8 +291,13 @@ template <int FN, int FM, int U, int RS>
 static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)((a.n + FN * 16 - 1) / (FN * 16)));
     constexpr int TK = RS > 0 && FN * FM <= 4 ? kMaxTSlices / RS : 1;  // partial sums of T the epilogue adds
+    constexpr int UG = U > 4 ? U / 2 : U;
     if (a.acc)
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true>), grid, dim3(256), 0, stream, a);
+    else if (a.group && TK > 1 && a.tks > 1)  // group-wise: half the pieces in flight, which leaves room for their scales
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, TK, 4, true>), grid, dim3(256), 0, stream, a);
+    else if (a.group)
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, 1, 4, true>), grid, dim3(256), 0, stream, a);
     else if (TK > 1 && a.tks > 1)
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false, TK>), grid, dim3(256), 0, stream, a);
     else
@@ -278,6 +349,64 @@ __host__ __device__ __forceinline__ int64_t xcd_order(int64_t bid, int64_t ntile
 // Epilogue of the many-token kernels for a wave's FN x FM tiles of 16 x 16, the wave
 // at (wn, wm) of a BN x BM CTA tile at (ch0, tok0): dequantize, add the low-rank
 // branch, store fp16 (or the exact integer sum).
+// Second half of the many-token epilogue, from the dequantized residual y: add the
+// low-rank branch and store fp16.
+template <int BN, int BM, int WN, int WM, bool LR4, int FN, int FM>
+__device__ __forceinline__ void pf_finish(const DualArgs &a, v4f (&y)[FN][FM], int64_t ch0, int64_t tok0, int wn, int wm,
+                                          int li, int g) {
+    if constexpr (LR4) {
+        // int4 low-rank branch: y += s_H (Q_H Q_L2^T)
+        if (a.r > 0) {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const int64_t chr = ch0 + wn * (BN / WN) + fn * 16 + li;
+                    const int64_t tokr = tok0 + wm * (BM / WM) + fm * 16 + li;
+                    const v4i acc2 = lr4_tile(a, chr, tokr, g);
+                    const float shv = a.sh[tokr < a.b ? tokr : a.b - 1];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) y[fn][fm][v] += shv * (float)(acc2[v] >> 8);
+                }
+        }
+    }
+    // fp16 low-rank branch: y += L2^T (channels x ranks) . T^T (ranks x tokens)
+    for (int k0 = 0; k0 < (LR4 ? 0 : a.r); k0 += 32) {
+        const int rank = k0 + g * 8;
+        const bool live = rank < a.r;  // r is a multiple of 16: live means rank + 8 <= r
+        const int rk = live ? rank : 0;
+        v8h la[FN], tb[FM];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + li;
+            la[fn] = load_h8(a.l2t + (ch < a.n ? ch : a.n - 1) * a.r + rk);
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
+            const float4 *tp = reinterpret_cast<const float4 *>(a.t + (tok < a.b ? tok : a.b - 1) * a.r + rk);
+            tb[fm] = live ? f32x8_to_h8(tp[0], tp[1]) : v8h{};
+        }
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) y[fn][fm] = mfma_f16(la[fn], tb[fm], y[fn][fm]);
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + 4 * g;
+            const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
+            if (ch < a.n && tok < a.b) {
+                v4h o;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) o[v] = (_Float16)y[fn][fm][v];
+                *reinterpret_cast<v4h *>(a.y + tok * a.n + ch) = o;
+            }
+        }
+}
+
 template <int BN, int BM, int WN, int WM, bool STORE_ACC, bool LR4, int FN, int FM>
 __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM], int64_t ch0, int64_t tok0, int wn, int wm,
                                             int li, int g) {
@@ -309,65 +438,22 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 #pragma unroll
                 for (int v = 0; v < 4; ++v) y[fn][fm][v] = (sxv[fm] * swv[v]) * (float)(acc[fn][fm][v] >> 8);
         }
-        if constexpr (LR4) {
-            // int4 low-rank branch: y += s_H (Q_H Q_L2^T)
-            if (a.r > 0) {
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-                    for (int fm = 0; fm < FM; ++fm) {
-                        const int64_t chr = ch0 + wn * (BN / WN) + fn * 16 + li;
-                        const int64_t tokr = tok0 + wm * (BM / WM) + fm * 16 + li;
-                        const v4i acc2 = lr4_tile(a, chr, tokr, g);
-                        const float shv = a.sh[tokr < a.b ? tokr : a.b - 1];
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) y[fn][fm][v] += shv * (float)(acc2[v] >> 8);
-                    }
-            }
-        }
-        // fp16 low-rank branch: y += L2^T (channels x ranks) . T^T (ranks x tokens)
-        for (int k0 = 0; k0 < (LR4 ? 0 : a.r); k0 += 32) {
-            const int rank = k0 + g * 8;
-            const bool live = rank < a.r;  // r is a multiple of 16: live means rank + 8 <= r
-            const int rk = live ? rank : 0;
-            v8h la[FN], tb[FM];
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + li;
-                la[fn] = load_h8(a.l2t + (ch < a.n ? ch : a.n - 1) * a.r + rk);
-            }
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
-                const float4 *tp = reinterpret_cast<const float4 *>(a.t + (tok < a.b ? tok : a.b - 1) * a.r + rk);
-                tb[fm] = live ? f32x8_to_h8(tp[0], tp[1]) : v8h{};
-            }
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) y[fn][fm] = mfma_f16(la[fn], tb[fm], y[fn][fm]);
-        }
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + 4 * g;
-                const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
-                if (ch < a.n && tok < a.b) {
-                    v4h o;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) o[v] = (_Float16)y[fn][fm][v];
-                    *reinterpret_cast<v4h *>(a.y + tok * a.n + ch) = o;
-                }
-            }
+        pf_finish<BN, BM, WN, WM, LR4>(a, y, ch0, tok0, wn, wm, li, g);
     }
 }
 
 // Three CTAs per compute unit (12 waves) fit the LDS ring; the register budget that
 // allows is asked for explicitly (measured 7-11% faster than two CTAs on the prefill
-// shapes).
-template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false>
-__global__ __launch_bounds__(WN * WM * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
+// shapes). The group-wise variant (GRP) keeps a second, fp32 set of accumulators and
+// runs two CTAs per unit.
+//
+// GRP (groups of kGroup = 128 along K): a stage is one group. Each slot of the ring
+// also holds the stage's scales, s_W of the tile's BN channels and s_X of its BM tokens
+// (one 4-byte direct-to-LDS load per thread, from the group-major scale arrays), and
+// each stage's integer sums are formed from zero and added to the fp32 accumulators
+// times s_X s_W.
+template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false>
+__global__ __launch_bounds__(WN * WM * 64, GRP ? 2 : 3)
 void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     constexpr int NT = WN * WM * 64;
     constexpr int FN = BN / (16 * WN), FM = BM / (16 * WM);
@@ -377,8 +463,12 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     constexpr int BLK = 16 * RB;                // one block of 16 rows
     constexpr int STAGE_BYTES = ROWS * RB;
     constexpr int DPT = ROWS * CPR / NT;        // 16-byte DMA loads per thread per stage
+    constexpr int LPT = DPT + (GRP ? 1 : 0);    // all loads per thread per stage
+    constexpr int SLOT = STAGE_BYTES + (GRP ? 4 * (BN + BM) : 0);
     static_assert(ROWS * 4 % NT == 0 && FN >= 1 && FM >= 1, "tile shape");
-    static_assert((S - 2) * DPT < 64, "outstanding loads fit vmcnt");
+    static_assert((S - 2) * LPT < 64, "outstanding loads fit vmcnt");
+    static_assert(!GRP || (RB == 64 && BN == 128 && BM == 128 && NT == 256 && !STORE_ACC && !LR4),
+                  "group-wise: one group per stage, one scale load per thread");
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int li = lane & 15, g = lane >> 4;
@@ -418,26 +508,50 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
         }
         off[j] = (uint32_t)(rel * kb + chunk * 16);
     }
-    __shared__ __attribute__((aligned(16))) uint8_t ring[S * STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[S * SLOT];
+    // GRP: this thread's scale: waves 0-1 load s_W of channel ch0 + tid, waves 2-3 s_X of
+    // token tok0 + tid - 128 (rows past n or b clamped), into the slot's scale area
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t soff = 0;
+    if constexpr (GRP) {
+        const int64_t rel = tid < BN ? (ch0 + tid < a.n ? tid : a.n - 1 - ch0)
+                                     : (tok0 + tid - BN < a.b ? tid - BN : a.b - 1 - tok0);
+        soff = (uint32_t)(rel * 4);
+    }
     // buffer loads straight to LDS: one resource per operand tile (raw, 32-bit element
     // format; every offset stays inside the tile's clamped rows), the per-lane offset
     // in a VGPR that never changes and the stage offset in an SGPR
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wbase), 0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xbase), 0, 0x7fffffff, 0x00020000);
     auto issue = [&](int st, auto slot) {
-        uint8_t *dst = ring + decltype(slot)::value * STAGE_BYTES;
+        uint8_t *dst = ring + decltype(slot)::value * SLOT;
 #pragma unroll
         for (int j = 0; j < DPT; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds((j * NT) / CPR < BN ? rw : rx,
                                                      (__attribute__((address_space(3))) void *)(dst + (j * NT + wave * kWave) * 16),
                                                      16, (int)off[j], st * RB, 0, 0);
+        if constexpr (GRP) {
+            // group st's row of the group-major scales, from the tile's first channel or token
+            const float *sb = wave_u < BN / kWave ? a.sw + (int64_t)st * a.n + ch0 : a.sx + (int64_t)st * a.b + tok0;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(sb), 0, 0x7fffffff, 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(dst + STAGE_BYTES + wave_u * kWave * 4),
+                                                     4, (int)soff, 0, 0, 0);
+        }
     };
 
     v4i acc[FN][FM];
+    v4f yg[GRP ? FN : 1][GRP ? FM : 1];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = v4i{0, 0, 0, 0};
+        for (int fm = 0; fm < FM; ++fm) {
+            acc[fn][fm] = v4i{0, 0, 0, 0};
+            if constexpr (GRP) yg[fn][fm] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    // GRP: this lane's scale reads in a slot: s_W of channels wn BN/WN + 16 fn + 4g..+3,
+    // s_X of token wm BM/WM + 16 fm + li
+    const uint32_t rsw = lds_offset(ring) + STAGE_BYTES + (wn * (BN / WN) + 4 * g) * 4;
+    const uint32_t rsx = lds_offset(ring) + STAGE_BYTES + (BN + wm * (BM / WM) + li) * 4;
 
     // this lane's operand addresses, per MFMA k-step h of a stage: FN weight blocks from
     // rda[h], FM token blocks from rdb[h]. Row li, chunk c of a block: with 64-byte rows,
@@ -464,14 +578,17 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
             const int st = s0 + u, c = st - (S - 1);
             if (c >= nst) return;
             if (c >= 0) {
-                wait_vmcnt<(S - 2) * DPT>();
+                wait_vmcnt<(S - 2) * LPT>();
                 stage_barrier();  // stage c landed for every thread; stage c - 1 consumed by every wave
             }
             issue(st < nst ? st : nst - 1, u);
             if (c < 0) return;
+            constexpr int OFF = ((u + 1) % S) * SLOT;  // slot of stage c
+            v4f swr[4];
+            float sxr[4];
+            if constexpr (GRP) lds_read_scales<OFF>(rsw, rsx, swr, sxr);
 #pragma unroll
             for (int h = 0; h < KS; ++h) {
-                constexpr int OFF = ((u + 1) % S) * STAGE_BYTES;  // slot of stage c
                 v4i raw[8];
                 lds_read_4x4<OFF, BLK>(rda[h], rdb[h], raw);
                 v4i alo[FN], ahi[FN], blo[FM], bhi[FM];
@@ -483,14 +600,26 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
                 for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
                     for (int fm = 0; fm < FM; ++fm) {
-                        acc[fn][fm] = mfma_i8(alo[fn], blo[fm], acc[fn][fm]);
-                        acc[fn][fm] = mfma_i8(ahi[fn], bhi[fm], acc[fn][fm]);
+                        if constexpr (GRP) {
+                            // the group's sum from zero, scaled in (2^-8 undoes the x16 x16 of the operands)
+                            v4i p = mfma_i8(alo[fn], blo[fm], v4i{0, 0, 0, 0});
+                            p = mfma_i8(ahi[fn], bhi[fm], p);
+                            const float sxs = sxr[fm] * 0x1p-8f;
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) yg[fn][fm][v] += (float)p[v] * (sxs * swr[fn][v]);
+                        } else {
+                            acc[fn][fm] = mfma_i8(alo[fn], blo[fm], acc[fn][fm]);
+                            acc[fn][fm] = mfma_i8(ahi[fn], bhi[fm], acc[fn][fm]);
+                        }
                     }
             }
         });
     }
 
-    pf_epilogue<BN, BM, WN, WM, STORE_ACC, LR4>(a, acc, ch0, tok0, wn, wm, li, g);
+    if constexpr (GRP)
+        pf_finish<BN, BM, WN, WM, false>(a, yg, ch0, tok0, wn, wm, li, g);
+    else
+        pf_epilogue<BN, BM, WN, WM, STORE_ACC, LR4>(a, acc, ch0, tok0, wn, wm, li, g);
 }
 
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB>
@@ -499,6 +628,9 @@ static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)(tiles_n * tiles_m)), block(WN * WM * 64);
     if (a.acc)
         hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, true>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
+    else if (a.group)
+        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, false, false, true>), grid, block, 0, stream, a, (int)tiles_n,
+                           (int)tiles_m);
     else if (a.lr4)
         hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, false, true>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
     else

@@ -68,6 +68,35 @@ __global__ __launch_bounds__(kPackThreads) void pack_weight_kernel(const float *
     }
 }
 
+// Group-wise packing (groups of kGroup = 128 along K, as in TwinQuant page 1, section
+// 5.1): one CTA per row, each thread one 8-element chunk at a time. A group is 16
+// chunks held by 16 consecutive lanes, so its amax is a 16-lane reduction and the
+// group's scale goes to sw[group][row] (group-major).
+__global__ __launch_bounds__(kPackThreads) void pack_weight_grouped_kernel(const float *w, int64_t n, int64_t m,
+                                                                           uint8_t *qw, float *sw) {
+    static_assert(kGroup == 128, "a group is 16 chunks of 8");
+    const int64_t j = blockIdx.x;
+    const int64_t nch = m / 8;  // a multiple of 16
+    const float4 *wr = reinterpret_cast<const float4 *>(w + j * m);
+    uint32_t *qr = reinterpret_cast<uint32_t *>(qw + j * (m / 2));
+    for (int64_t c = threadIdx.x; c < nch; c += kPackThreads) {  // whole 16-lane groups enter together
+        const float4 va = wr[2 * c], vb = wr[2 * c + 1];
+        float mx = absmax8_f32(va, vb, 0.0f);
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, off, kWave));
+        const float s = mx / kQMax;
+        if ((threadIdx.x & 15) == 0) sw[(c / 16) * n + j] = s;
+        qr[c] = mx == 0.0f ? 0u : quant8_f32(va, vb, s);
+    }
+}
+
+hipError_t launch_pack_weight_grouped(const float *w, int64_t n, int64_t m, uint8_t *qw, float *sw,
+                                      hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_weight_grouped_kernel, dim3((unsigned)n), dim3(kPackThreads), 0, stream, w, n, m, qw, sw);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack_weight(const float *w, int64_t n, int64_t m, uint8_t *qw, float *sw, hipStream_t stream) {
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)n), dim3(kPackThreads), 0, stream, w, m, qw, sw);

@@ -42,16 +42,129 @@ struct LinearLayout {
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-LinearLayout linear_layout(int64_t b, int64_t m, int64_t n, int64_t r) {
+// group: 0 (one scale per token) or twq::kGroup (s_X group-major [m / kGroup][b])
+LinearLayout linear_layout(int64_t b, int64_t m, int64_t n, int64_t r, int group) {
     LinearLayout L{};
     L.plan = twq::plan_act(b, m, r);
     L.direct = r > 0 && L.plan.mode == 1 && L.plan.ks > 1 && L.plan.ks <= twq::dual_max_t_slices(b, n, (int)r);
     L.qx = 0;
     L.sx = align256((size_t)(b * m / 2));
-    L.t = L.sx + align256((size_t)b * 4);
+    L.t = L.sx + align256((size_t)b * 4 * (size_t)(group ? m / group : 1));
     L.partials = L.t + (L.direct ? 0 : align256((size_t)(b * r) * 4));
     L.total = L.partials + align256(L.plan.workspace_bytes);
     return L;
+}
+
+bool valid_group(int64_t g) { return g == twq::kGroup; }
+
+// The entry points with and without group-wise scales share these bodies; group is 0
+// or twq::kGroup and has been validated.
+twq_status quantize_act_impl(const void *x, int64_t b, int64_t m, int group, void *qx, float *sx, const void *l1t,
+                             int64_t r, float *t, void *workspace, size_t workspace_bytes, void *stream,
+                             const char *name) {
+    if (!valid_b(b) || !valid_m(m) || !valid_r(r)) return TWQ_ERR_SHAPE;
+    if (b == 0) return TWQ_OK;
+    if (!x || !qx || !sx) return TWQ_ERR_NULL;
+    if (r > 0 && (!l1t || !t)) return TWQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(qx) || !aligned16(sx)) return TWQ_ERR_ALIGN;
+    if (r > 0 && (!aligned16(l1t) || !aligned16(t))) return TWQ_ERR_ALIGN;
+    const twq::ActPlan plan = twq::plan_act(b, m, r);
+    if (r > 0 && plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.workspace_bytes) return TWQ_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return TWQ_ERR_ALIGN;
+    }
+    twq::ActArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.b = b;
+    a.m = m;
+    a.qx = static_cast<uint8_t *>(qx);
+    a.sx = sx;
+    a.l1t = static_cast<const uint16_t *>(l1t);
+    a.r = (int)r;
+    a.t = t;
+    a.group = group;
+    if (r > 0 && plan.workspace_bytes > 0) a.partials = static_cast<float *>(workspace);
+    const hipError_t e = twq::launch_act(a, plan, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, name);
+}
+
+twq_status dual_linear_impl(const void *qx, const float *sx, const void *qw, const float *sw, const float *t,
+                            const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n, int group,
+                            void *stream, const char *name) {
+    if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return TWQ_ERR_SHAPE;
+    if (b == 0 || n == 0) return TWQ_OK;
+    if (!qx || !sx || !qw || !sw || !y) return TWQ_ERR_NULL;
+    if (r > 0 && (!t || !l2t)) return TWQ_ERR_NULL;
+    if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(sw) || !aligned16(y))
+        return TWQ_ERR_ALIGN;
+    if (r > 0 && (!aligned16(t) || !aligned16(l2t))) return TWQ_ERR_ALIGN;
+    twq::DualArgs a{};
+    a.qx = static_cast<const uint8_t *>(qx);
+    a.sx = sx;
+    a.qw = static_cast<const uint8_t *>(qw);
+    a.sw = sw;
+    a.t = t;
+    a.tpart = t;
+    a.tks = 1;
+    a.l2t = static_cast<const uint16_t *>(l2t);
+    a.r = (int)r;
+    a.y = static_cast<uint16_t *>(y);
+    a.b = b;
+    a.m = m;
+    a.n = n;
+    a.group = group;
+    const hipError_t e = twq::launch_dual_linear(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, name);
+}
+
+twq_status linear_impl(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t, int64_t r,
+                       void *y, int64_t b, int64_t m, int64_t n, int group, void *workspace, size_t workspace_bytes,
+                       void *stream, const char *name) {
+    if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return TWQ_ERR_SHAPE;
+    if (b == 0 || n == 0) return TWQ_OK;
+    if (!x || !qw || !sw || !y) return TWQ_ERR_NULL;
+    if (r > 0 && (!l1t || !l2t)) return TWQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(qw) || !aligned16(sw) || !aligned16(y)) return TWQ_ERR_ALIGN;
+    if (r > 0 && (!aligned16(l1t) || !aligned16(l2t))) return TWQ_ERR_ALIGN;
+    const LinearLayout L = linear_layout(b, m, n, r, group);
+    if (!workspace || workspace_bytes < L.total) return TWQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return TWQ_ERR_ALIGN;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+
+    twq::ActArgs act{};
+    act.x = static_cast<const uint16_t *>(x);
+    act.b = b;
+    act.m = m;
+    act.qx = ws + L.qx;
+    act.sx = reinterpret_cast<float *>(ws + L.sx);
+    act.l1t = static_cast<const uint16_t *>(l1t);
+    act.r = (int)r;
+    act.t = reinterpret_cast<float *>(ws + L.t);
+    act.partials = reinterpret_cast<float *>(ws + L.partials);
+    act.keep_partials = L.direct;
+    act.group = group;
+    hipError_t e = twq::launch_act(act, L.plan, st);
+    if (e != hipSuccess) return hip_fail(e, name);
+
+    twq::DualArgs a{};
+    a.qx = act.qx;
+    a.sx = act.sx;
+    a.qw = static_cast<const uint8_t *>(qw);
+    a.sw = sw;
+    a.t = act.t;
+    a.tpart = L.direct ? act.partials : act.t;
+    a.tks = L.direct ? L.plan.ks : 1;
+    a.tstride = L.direct ? (int64_t)L.plan.fm * 16 * r : 0;
+    a.l2t = static_cast<const uint16_t *>(l2t);
+    a.r = (int)r;
+    a.y = static_cast<uint16_t *>(y);
+    a.b = b;
+    a.m = m;
+    a.n = n;
+    a.group = group;
+    e = twq::launch_dual_linear(a, st);
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, name);
 }
 
 }  // namespace
@@ -82,29 +195,15 @@ size_t twq_quantize_act_workspace_bytes(int64_t b, int64_t m, int64_t r) {
 
 twq_status twq_quantize_act(const void *x, int64_t b, int64_t m, void *qx, float *sx, const void *l1t,
                             int64_t r, float *t, void *workspace, size_t workspace_bytes, void *stream) {
-    if (!valid_b(b) || !valid_m(m) || !valid_r(r)) return TWQ_ERR_SHAPE;
-    if (b == 0) return TWQ_OK;
-    if (!x || !qx || !sx) return TWQ_ERR_NULL;
-    if (r > 0 && (!l1t || !t)) return TWQ_ERR_NULL;
-    if (!aligned16(x) || !aligned16(qx) || !aligned16(sx)) return TWQ_ERR_ALIGN;
-    if (r > 0 && (!aligned16(l1t) || !aligned16(t))) return TWQ_ERR_ALIGN;
-    const twq::ActPlan plan = twq::plan_act(b, m, r);
-    if (r > 0 && plan.workspace_bytes > 0) {
-        if (!workspace || workspace_bytes < plan.workspace_bytes) return TWQ_ERR_WORKSPACE;
-        if (!aligned16(workspace)) return TWQ_ERR_ALIGN;
-    }
-    twq::ActArgs a{};
-    a.x = static_cast<const uint16_t *>(x);
-    a.b = b;
-    a.m = m;
-    a.qx = static_cast<uint8_t *>(qx);
-    a.sx = sx;
-    a.l1t = static_cast<const uint16_t *>(l1t);
-    a.r = (int)r;
-    a.t = t;
-    if (r > 0 && plan.workspace_bytes > 0) a.partials = static_cast<float *>(workspace);
-    const hipError_t e = twq::launch_act(a, plan, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_quantize_act");
+    return quantize_act_impl(x, b, m, 0, qx, sx, l1t, r, t, workspace, workspace_bytes, stream, "twq_quantize_act");
+}
+
+twq_status twq_quantize_act_grouped(const void *x, int64_t b, int64_t m, int64_t g, void *qx, float *sx,
+                                    const void *l1t, int64_t r, float *t, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+    if (!valid_group(g)) return TWQ_ERR_UNSUPPORTED;
+    return quantize_act_impl(x, b, m, (int)g, qx, sx, l1t, r, t, workspace, workspace_bytes, stream,
+                             "twq_quantize_act_grouped");
 }
 
 twq_status twq_pack_weight(const float *w_res, int64_t n, int64_t m, void *qw, float *sw, void *stream) {
@@ -117,31 +216,28 @@ twq_status twq_pack_weight(const float *w_res, int64_t n, int64_t m, void *qw, f
     return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_pack_weight");
 }
 
+twq_status twq_pack_weight_grouped(const float *w_res, int64_t n, int64_t m, int64_t g, void *qw, float *sw,
+                                   void *stream) {
+    if (!valid_group(g)) return TWQ_ERR_UNSUPPORTED;
+    if (!valid_n(n) || !valid_m(m)) return TWQ_ERR_SHAPE;
+    if (n == 0) return TWQ_OK;
+    if (!w_res || !qw || !sw) return TWQ_ERR_NULL;
+    if (!aligned16(w_res) || !aligned16(qw) || !aligned16(sw)) return TWQ_ERR_ALIGN;
+    const hipError_t e = twq::launch_pack_weight_grouped(w_res, n, m, static_cast<uint8_t *>(qw), sw,
+                                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_pack_weight_grouped");
+}
+
 twq_status twq_dual_linear(const void *qx, const float *sx, const void *qw, const float *sw, const float *t,
                            const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n, void *stream) {
-    if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return TWQ_ERR_SHAPE;
-    if (b == 0 || n == 0) return TWQ_OK;
-    if (!qx || !sx || !qw || !sw || !y) return TWQ_ERR_NULL;
-    if (r > 0 && (!t || !l2t)) return TWQ_ERR_NULL;
-    if (!aligned16(qx) || !aligned16(sx) || !aligned16(qw) || !aligned16(sw) || !aligned16(y))
-        return TWQ_ERR_ALIGN;
-    if (r > 0 && (!aligned16(t) || !aligned16(l2t))) return TWQ_ERR_ALIGN;
-    twq::DualArgs a{};
-    a.qx = static_cast<const uint8_t *>(qx);
-    a.sx = sx;
-    a.qw = static_cast<const uint8_t *>(qw);
-    a.sw = sw;
-    a.t = t;
-    a.tpart = t;
-    a.tks = 1;
-    a.l2t = static_cast<const uint16_t *>(l2t);
-    a.r = (int)r;
-    a.y = static_cast<uint16_t *>(y);
-    a.b = b;
-    a.m = m;
-    a.n = n;
-    const hipError_t e = twq::launch_dual_linear(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_dual_linear");
+    return dual_linear_impl(qx, sx, qw, sw, t, l2t, r, y, b, m, n, 0, stream, "twq_dual_linear");
+}
+
+twq_status twq_dual_linear_grouped(const void *qx, const float *sx, const void *qw, const float *sw, const float *t,
+                                   const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n, int64_t g,
+                                   void *stream) {
+    if (!valid_group(g)) return TWQ_ERR_UNSUPPORTED;
+    return dual_linear_impl(qx, sx, qw, sw, t, l2t, r, y, b, m, n, (int)g, stream, "twq_dual_linear_grouped");
 }
 
 twq_status twq_debug_residual_acc(const void *qx, const void *qw, int32_t *acc, int64_t b, int64_t m, int64_t n,
@@ -220,54 +316,25 @@ twq_status twq_dual_linear_lr4(const void *qx, const float *sx, const void *qw, 
 
 size_t twq_linear_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r) {
     if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return 0;
-    return linear_layout(b, m, n, r).total;
+    return linear_layout(b, m, n, r, 0).total;
 }
 
 twq_status twq_linear(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t, int64_t r,
                       void *y, int64_t b, int64_t m, int64_t n, void *workspace, size_t workspace_bytes, void *stream) {
-    if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return TWQ_ERR_SHAPE;
-    if (b == 0 || n == 0) return TWQ_OK;
-    if (!x || !qw || !sw || !y) return TWQ_ERR_NULL;
-    if (r > 0 && (!l1t || !l2t)) return TWQ_ERR_NULL;
-    if (!aligned16(x) || !aligned16(qw) || !aligned16(sw) || !aligned16(y)) return TWQ_ERR_ALIGN;
-    if (r > 0 && (!aligned16(l1t) || !aligned16(l2t))) return TWQ_ERR_ALIGN;
-    const LinearLayout L = linear_layout(b, m, n, r);
-    if (!workspace || workspace_bytes < L.total) return TWQ_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return TWQ_ERR_ALIGN;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    const hipStream_t st = static_cast<hipStream_t>(stream);
+    return linear_impl(x, qw, sw, l1t, l2t, r, y, b, m, n, 0, workspace, workspace_bytes, stream, "twq_linear");
+}
 
-    twq::ActArgs act{};
-    act.x = static_cast<const uint16_t *>(x);
-    act.b = b;
-    act.m = m;
-    act.qx = ws + L.qx;
-    act.sx = reinterpret_cast<float *>(ws + L.sx);
-    act.l1t = static_cast<const uint16_t *>(l1t);
-    act.r = (int)r;
-    act.t = reinterpret_cast<float *>(ws + L.t);
-    act.partials = reinterpret_cast<float *>(ws + L.partials);
-    act.keep_partials = L.direct;
-    hipError_t e = twq::launch_act(act, L.plan, st);
-    if (e != hipSuccess) return hip_fail(e, "twq_linear (activations)");
+size_t twq_linear_grouped_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r, int64_t g) {
+    if (!valid_group(g) || !valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return 0;
+    return linear_layout(b, m, n, r, (int)g).total;
+}
 
-    twq::DualArgs a{};
-    a.qx = act.qx;
-    a.sx = act.sx;
-    a.qw = static_cast<const uint8_t *>(qw);
-    a.sw = sw;
-    a.t = act.t;
-    a.tpart = L.direct ? act.partials : act.t;
-    a.tks = L.direct ? L.plan.ks : 1;
-    a.tstride = L.direct ? (int64_t)L.plan.fm * 16 * r : 0;
-    a.l2t = static_cast<const uint16_t *>(l2t);
-    a.r = (int)r;
-    a.y = static_cast<uint16_t *>(y);
-    a.b = b;
-    a.m = m;
-    a.n = n;
-    e = twq::launch_dual_linear(a, st);
-    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_linear");
+twq_status twq_linear_grouped(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t,
+                              int64_t r, void *y, int64_t b, int64_t m, int64_t n, int64_t g, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    if (!valid_group(g)) return TWQ_ERR_UNSUPPORTED;
+    return linear_impl(x, qw, sw, l1t, l2t, r, y, b, m, n, (int)g, workspace, workspace_bytes, stream,
+                       "twq_linear_grouped");
 }
 
 }  // extern "C"

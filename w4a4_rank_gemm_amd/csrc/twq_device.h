@@ -195,4 +195,27 @@ __device__ __forceinline__ void lds_read_4(uint32_t a, v4i (&r)[4]) {
         : "memory");
 }
 
+// Group scales of one ring stage for a wave's 4 x 4 tiles of 16 x 16: four 16-byte reads
+// from address w (s_W of channels 4g..4g+3 of each of four channel blocks, 64 bytes
+// apart) and four 4-byte reads from address x (s_X of token li of each of four token
+// blocks, 64 bytes apart), each plus OFF, completed before returning for the same
+// reason and in the same way as lds_read_4x4.
+template <int OFF>
+__device__ __forceinline__ void lds_read_scales(uint32_t w, uint32_t x, v4f (&sw)[4], float (&sx)[4]) {
+    static_assert(OFF >= 0 && OFF + 192 < 65536, "ds_read immediate offset");
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%10\n\t"
+        "ds_read_b128 %1, %8 offset:%11\n\t"
+        "ds_read_b128 %2, %8 offset:%12\n\t"
+        "ds_read_b128 %3, %8 offset:%13\n\t"
+        "ds_read_b32 %4, %9 offset:%10\n\t"
+        "ds_read_b32 %5, %9 offset:%11\n\t"
+        "ds_read_b32 %6, %9 offset:%12\n\t"
+        "ds_read_b32 %7, %9 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(sw[0]), "=v"(sw[1]), "=v"(sw[2]), "=v"(sw[3]), "=v"(sx[0]), "=v"(sx[1]), "=v"(sx[2]), "=v"(sx[3])
+        : "v"(w), "v"(x), "n"(OFF), "n"(OFF + 64), "n"(OFF + 128), "n"(OFF + 192)
+        : "memory");
+}
+
 }  // namespace twq

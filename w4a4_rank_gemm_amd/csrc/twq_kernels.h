@@ -36,13 +36,21 @@ struct ActArgs {
     float *t;
     float *partials;  // ks > 1: [ks][rows_pad][r], rows_pad = 128 row_tiles (mode 0) or 16 fm (mode 1)
     int keep_partials;  // ks > 1: leave T as partial sums (the caller's dual launch adds them)
+    int group;          // 0: one scale per token row, s_X [b]; kGroup: one scale per kGroup
+                        // consecutive elements of a row, s_X group-major [m / kGroup][b]
 };
+
+// Group size of the group-wise variant: one K stage of every main loop.
+constexpr int kGroup = 128;
 
 hipError_t launch_act(const ActArgs &a, const ActPlan &plan, hipStream_t stream);
 // ---- weight packer -----------------------------------------------------------------
 
 hipError_t launch_pack_weight(const float *w, int64_t n, int64_t m, uint8_t *qw, float *sw,
                               hipStream_t stream);
+// group-wise: s_W group-major [m / kGroup][n]
+hipError_t launch_pack_weight_grouped(const float *w, int64_t n, int64_t m, uint8_t *qw, float *sw,
+                                      hipStream_t stream);
 
 // ---- fused dual linear ----------------------------------------------------------------
 
@@ -64,6 +72,7 @@ struct DualArgs {
     const uint8_t *qh; // [b][r/2] packed Q_H
     const float *sh;   // [b]
     const uint8_t *ql2;// [n][r/2] packed Q_L2
+    int group;         // kGroup: group-wise scales, sx [m / kGroup][b] and sw [m / kGroup][n]
 };
 
 hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream);
