@@ -48,6 +48,17 @@ def dual_linear_bytes(b, m, n, r):
     return b * m // 2 + 4 * b + m * n // 2 + 4 * n + 4 * b * r + 2 * n * r + 2 * b * n
 
 
+def call_bytes_grouped(b, m, n, r, g):
+    """Compulsory HBM bytes of one group-wise call: as call_bytes, with one s_W per group."""
+    return 2 * b * m + m * n // 2 + 4 * n * (m // g) + 2 * r * (m + n) + 2 * b * n
+
+
+def dual_linear_grouped_bytes(b, m, n, r, g):
+    """Algorithmic bytes of one twq_dual_linear_grouped launch: Q_X, the m/g scales per
+    token and per channel, Q_W, T and L2 read once, Y written once."""
+    return b * m // 2 + 4 * b * (m // g) + m * n // 2 + 4 * n * (m // g) + 4 * b * r + 2 * n * r + 2 * b * n
+
+
 def call_bytes_lr4(b, m, n, r):
     """Compulsory HBM bytes of one call with the int4 low-rank branch: X fp16, Q_W, s_W,
     Q_L1 and Q_L2 (4-bit), c, Y fp16."""
@@ -93,6 +104,39 @@ def lowrank_storage_ratio(m, n, r):
     return 2 * r * (m + n) / (m * n / 2)
 
 
+def _cpu_baseline_grouped(d, g, budget_s=12.0):
+    """The group-wise oracle on the host, weights pre-quantized, on the first rows of the
+    batch (the per-group integer sums of every row would not fit in memory at full size);
+    the rate scales with the rows it covered."""
+    import numpy as np
+
+    import oracle
+    x, w, l1t, l2t = d["x"], d["w_res"], d["l1t"], d["l2t"]
+    b, m = x.shape
+    n, r = w.shape[0], l1t.shape[0]
+    rows = int(min(b, max(1, (256 << 20) // (n * (m // g) * 8))))
+    xs = np.ascontiguousarray(x[:rows])
+    qw, _, sw = oracle.quantize_weight_grouped(w, g)  # offline packing, not timed
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        qx, _, sx = oracle.quantize_act_grouped(xs, g)
+        accg = oracle.residual_acc_grouped(qx, qw, g)
+        y = np.einsum("ig,jg,ijg->ij", sx.astype(np.float64), sw.astype(np.float64), accg)
+        if r:
+            y += oracle.lowrank_out(oracle.lowrank_t(xs, l1t), l2t)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 1000:
+            break
+    sec = el / calls * b / rows
+    return {"value": layer_ops(b, m, n, r) / sec / 1e12, "unit": "TOPS", "cores": oracle.max_threads(),
+            "kind": "oracle", "ms_per_call": sec * 1e3,
+            "sample": f"{calls} calls on the first {rows} of {b} tokens (b={b}, m={m}, n={n}, r={r}, "
+                      f"groups of {g}) in {el:.1f} s, scaled to the whole batch; weights quantized once "
+                      "outside the timing"}
+
+
 def _cpu_baseline(d, budget_s=12.0, lr4=False):
     """The oracle (plain C, OpenMP) on the host: per-call work with weights pre-quantized."""
     import numpy as np
@@ -136,6 +180,8 @@ def main():
     ap.add_argument("--lowrank", choices=("fp16", "int4"), default="fp16",
                     help="fp16: the fp16 low-rank branch; int4: twq_quantize_act + twq_lowrank_requant "
                          "+ twq_dual_linear_lr4 with 4-bit L1, L2 and H")
+    ap.add_argument("--group", type=int, choices=(0, 128), default=0,
+                    help="128: group-wise scales (twq_*_grouped entry points, groups of 128 along K)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate over (0: auto)")
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
@@ -162,15 +208,19 @@ def main():
     d = synth.make_layer(cfg)
 
     lr4 = args.lowrank == "int4"
+    grp = args.group
     if lr4 and args.path != "linear":
         ap.error("--lowrank int4 has one call sequence; leave --path at its default")
-    per_copy = call_bytes_lr4(b, m, n, r) if lr4 else call_bytes(b, m, n, r)
+    if lr4 and grp:
+        ap.error("--group applies to the fp16 low-rank branch only")
+    per_copy = (call_bytes_lr4(b, m, n, r) if lr4 else call_bytes_grouped(b, m, n, r, grp) if grp
+                else call_bytes(b, m, n, r))
     copies = args.copies or max(1, math.ceil(ROTATE_BYTES / per_copy))
     x0 = torch.from_numpy(d["x"]).to(dev)
     w0 = torch.from_numpy(d["w_res"]).to(dev)
     l10 = torch.from_numpy(d["l1t"]).to(dev) if r else None
     l20 = torch.from_numpy(d["l2t"]).to(dev) if r else None
-    qw0, sw0 = twq.pack_weight(w0)
+    qw0, sw0 = twq.pack_weight_grouped(w0, grp) if grp else twq.pack_weight(w0)
     del w0
     lp0 = twq.pack_lowrank_int4(l10, l20) if (lr4 and r) else None
     sets = []
@@ -179,7 +229,7 @@ def main():
             "x": x0.clone(), "qw": qw0.clone(), "sw": sw0.clone(),
             "l1t": l10.clone() if (r and not lr4) else None, "l2t": l20.clone() if (r and not lr4) else None,
             "qx": torch.empty((b, m // 2), dtype=torch.uint8, device=dev),
-            "sx": torch.empty((b,), dtype=torch.float32, device=dev),
+            "sx": torch.empty((m // grp, b) if grp else (b,), dtype=torch.float32, device=dev),
             "t": torch.empty((b, r), dtype=torch.float32, device=dev) if (r and not lr4) else None,
             "y": torch.empty((b, n), dtype=torch.float16, device=dev),
         }
@@ -193,14 +243,23 @@ def main():
     del lp0
     L = twq.lib()
     ws, wsb = twq._workspace(dev, max(L.twq_quantize_act_workspace_bytes(b, m, r),
-                                      L.twq_linear_workspace_bytes(b, m, n, r)))
+                                      L.twq_linear_grouped_workspace_bytes(b, m, n, r, grp) if grp
+                                      else L.twq_linear_workspace_bytes(b, m, n, r)))
     P = lambda t: None if t is None else twq.ctypes.c_void_p(t.data_ptr())
 
     def layer(s, stream):
+        if grp:
+            twq._check(L.twq_linear_grouped(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["l1t"]), P(s["l2t"]), r,
+                                            P(s["y"]), b, m, n, grp, P(ws), wsb, stream), "twq_linear_grouped")
+            return
         twq._check(L.twq_linear(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["l1t"]), P(s["l2t"]), r, P(s["y"]),
                                 b, m, n, P(ws), wsb, stream), "twq_linear")
 
     def quant(s, stream):
+        if grp:
+            twq._check(L.twq_quantize_act_grouped(P(s["x"]), b, m, grp, P(s["qx"]), P(s["sx"]), P(s["l1t"]), r,
+                                                  P(s["t"]), P(ws), wsb, stream), "twq_quantize_act_grouped")
+            return
         twq._check(L.twq_quantize_act(P(s["x"]), b, m, P(s["qx"]), P(s["sx"]), P(s["l1t"]), 0 if lr4 else r,
                                       P(s["t"]), P(ws), wsb, stream), "twq_quantize_act")
         if lr4 and r:
@@ -212,6 +271,11 @@ def main():
             twq._check(L.twq_dual_linear_lr4(P(s["qx"]), P(s["sx"]), P(s["qw"]), P(s["sw"]), P(s["qh"]),
                                              P(s["sh"]), P(s["ql2"]), r, P(s["y"]), b, m, n, stream),
                        "twq_dual_linear_lr4")
+            return
+        if grp:
+            twq._check(L.twq_dual_linear_grouped(P(s["qx"]), P(s["sx"]), P(s["qw"]), P(s["sw"]), P(s["t"]),
+                                                 P(s["l2t"]), r, P(s["y"]), b, m, n, grp, stream),
+                       "twq_dual_linear_grouped")
             return
         twq._check(L.twq_dual_linear(P(s["qx"]), P(s["sx"]), P(s["qw"]), P(s["sw"]), P(s["t"]), P(s["l2t"]), r,
                                      P(s["y"]), b, m, n, stream), "twq_dual_linear")
@@ -291,9 +355,10 @@ def main():
     ops = layer_ops(b, m, n, r)
     tops = ops / (ms_step * 1e-3) / 1e12
     decode = b <= 64
-    kbytes = dual_linear_lr4_bytes(b, m, n, r) if lr4 else dual_linear_bytes(b, m, n, r)
-    cbytes = call_bytes_lr4(b, m, n, r) if lr4 else call_bytes(b, m, n, r)
-    traffic = None if lr4 else measured_traffic(args.config)
+    kbytes = (dual_linear_lr4_bytes(b, m, n, r) if lr4 else dual_linear_grouped_bytes(b, m, n, r, grp) if grp
+              else dual_linear_bytes(b, m, n, r))
+    cbytes = per_copy
+    traffic = None if (lr4 or grp) else measured_traffic(args.config)
     if decode:
         ach = kbytes / (us_dual * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -302,11 +367,18 @@ def main():
         ach = 2 * b * m * n / (us_dual * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": traffic}
-    roof["kernel"] = "twq_dual_linear_lr4" if lr4 else "twq_dual_linear"
+    roof["kernel"] = "twq_dual_linear_lr4" if lr4 else "twq_dual_linear_grouped" if grp else "twq_dual_linear"
     roof["kernel_us"] = round(us_dual, 3)
     roof["algorithmic_bytes"] = kbytes
     roof["algorithmic_int8_ops"] = 2 * b * m * n
 
+    sfx = "_grouped" if grp else ""
+    if lr4:
+        entry_points = "twq_quantize_act+twq_lowrank_requant+twq_dual_linear_lr4"
+    elif args.path == "linear":
+        entry_points = f"twq_linear{sfx}"
+    else:
+        entry_points = f"twq_quantize_act{sfx}+twq_dual_linear{sfx}"
     out = {
         "metric": BASELINE_METRIC,
         "value": round(tops, 3),
@@ -324,9 +396,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.config}: b={b} m={m} n={n} r={r}", "b": b, "m": m, "n": n, "r": r,
                    "weight_copies_rotated": copies, "launch": "eager" if args.eager else "hip_graph",
-                   "lowrank": args.lowrank,
-                   "entry_points": ("twq_quantize_act+twq_lowrank_requant+twq_dual_linear_lr4" if lr4 else
-                                    "twq_linear" if args.path == "linear" else "twq_quantize_act+twq_dual_linear"),
+                   "lowrank": args.lowrank, "group": grp or "per token / per channel",
+                   "entry_points": entry_points,
                    "call_bytes": cbytes,
                    "hbm_frac_whole_call": round(cbytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                    "int8_mfma_frac_whole_call": round(2 * b * m * n / (ms_step * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)},
@@ -334,7 +405,7 @@ def main():
     }
     if not args.no_cpu:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = _cpu_baseline(d, lr4=lr4)
+        out["cpu_baseline"] = _cpu_baseline_grouped(d, grp) if grp else _cpu_baseline(d, lr4=lr4)
         out["cpu_baseline"]["host"] = platform.processor() or platform.machine()
     print(json.dumps(out), flush=True)
 
