@@ -169,6 +169,120 @@ def _cpu_baseline(d, budget_s=12.0, lr4=False):
                       f"in {el:.1f} s; weights quantized once outside the timing"}
 
 
+def _graph_time(fn, steps, warmup, stream):
+    """GPU time per step (us) of `fn(i)` for i in range(steps), captured into a HIP graph on
+    `stream` and replayed once after an untimed replay of `warmup` steps."""
+    import torch
+    gw, g = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn(0)  # lazy initialisation outside the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gw, stream=stream):
+            for i in range(warmup):
+                fn(i)
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                fn(i)
+        gw.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        e1.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e3
+
+
+COMPARE_CONFIGS = ("o_proj_decode", "70b_gate_up_decode", "gate_up_prefill", "70b_gate_up_prefill")
+SWEEP_RANKS = (0, 32, 64, 128, 256)
+
+
+def compare(args):
+    """Context for the fused layer, one JSON line per measurement (weights rotated as in
+    the main benchmark, HIP graphs):
+      fused      twq_linear (quantize + T, then the fused main loop and epilogue);
+      unfused    the same pieces with the partial result spilled: twq_quantize_act (Q_X,
+                 s_X, T), the residual-only fused kernel writing Y_res to HBM, then T L2
+                 and Y_res + T L2 as two more launches (fp16 GEMM and add from the
+                 platform library);
+      residual   twq_linear with r = 0 (plain W4A4);
+      fp16       the dense fp16 layer Y = X W^T on the platform GEMM (hipBLASLt);
+    and a sweep of the rank r over SWEEP_RANKS on each shape (fused layer only; random
+    factors, which do not change the time)."""
+    import torch
+
+    import synth
+    import w4a4_rank_gemm_amd as twq
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)  # default priority
+    L = twq.lib()
+    P = lambda t: None if t is None else twq.ctypes.c_void_p(t.data_ptr())
+    hs = lambda: twq.ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    names = args.compare_configs.split(",") if args.compare_configs else COMPARE_CONFIGS
+    for name in names:
+        cfg = synth.CONFIGS[name]
+        b, m, n, r = cfg.b, cfg.m, cfg.n, cfg.r
+        gen = torch.Generator(device=dev).manual_seed(cfg.index)
+        x0 = (torch.randn((b, m), generator=gen, device=dev) * 2).half()
+        w0 = torch.randn((n, m), generator=gen, device=dev) * 0.02
+        qw0, sw0 = twq.pack_weight(w0)
+        w16_0 = w0.half()
+        del w0
+        copies = max(1, math.ceil(ROTATE_BYTES / call_bytes(b, m, n, max(SWEEP_RANKS))))
+        copies16 = max(1, math.ceil(ROTATE_BYTES / (2 * m * n)))
+        sets = [{"x": x0.clone(), "qw": qw0.clone(), "sw": sw0.clone(),
+                 "qx": torch.empty((b, m // 2), dtype=torch.uint8, device=dev),
+                 "sx": torch.empty((b,), dtype=torch.float32, device=dev),
+                 "y": torch.empty((b, n), dtype=torch.float16, device=dev)} for _ in range(copies)]
+        w16 = [w16_0.clone() for _ in range(copies16)]
+        del w16_0
+
+        def lowrank(rk):
+            for s_ in sets:
+                s_["l1t"] = (torch.randn((rk, m), generator=gen, device=dev) * 0.02).half() if rk else None
+                s_["l2t"] = (torch.randn((n, rk), generator=gen, device=dev) * 0.02).half() if rk else None
+                s_["t"] = torch.empty((b, rk), dtype=torch.float32, device=dev) if rk else None
+
+        ws, wsb = twq._workspace(dev, max(L.twq_linear_workspace_bytes(b, m, n, max(SWEEP_RANKS)),
+                                          L.twq_quantize_act_workspace_bytes(b, m, max(SWEEP_RANKS))))
+
+        def fused(rk):
+            def f(i):
+                s_ = sets[i % copies]
+                twq._check(L.twq_linear(P(s_["x"]), P(s_["qw"]), P(s_["sw"]), P(s_["l1t"]), P(s_["l2t"]), rk,
+                                        P(s_["y"]), b, m, n, P(ws), wsb, hs()), "twq_linear")
+            return f
+
+        def unfused(i):
+            s_ = sets[i % copies]
+            st = hs()
+            twq._check(L.twq_quantize_act(P(s_["x"]), b, m, P(s_["qx"]), P(s_["sx"]), P(s_["l1t"]), r, P(s_["t"]),
+                                          P(ws), wsb, st), "twq_quantize_act")
+            twq._check(L.twq_dual_linear(P(s_["qx"]), P(s_["sx"]), P(s_["qw"]), P(s_["sw"]), None, None, 0,
+                                         P(s_["y"]), b, m, n, st), "twq_dual_linear")
+            s_["y"].add_(torch.nn.functional.linear(s_["t"].half(), s_["l2t"]))
+
+        def fp16(i):
+            sets[i % copies]["y"].copy_(torch.nn.functional.linear(sets[i % copies]["x"], w16[i % copies16]))
+
+        def emit(variant, us, rk=r):
+            print(json.dumps({"compare": name, "variant": variant, "b": b, "m": m, "n": n, "r": rk,
+                              "us_per_call": round(us, 3), "effective_tops": round(layer_ops(b, m, n, rk) / us / 1e6, 2)}),
+                  flush=True)
+
+        lowrank(r)
+        emit("fused", _graph_time(fused(r), args.steps, args.warmup, stream))
+        emit("unfused", _graph_time(unfused, args.steps, args.warmup, stream))
+        emit("residual", _graph_time(fused(0), args.steps, args.warmup, stream), 0)
+        emit("fp16", _graph_time(fp16, args.steps, args.warmup, stream), 0)
+        for rk in SWEEP_RANKS:
+            lowrank(rk)
+            emit("fused_rank_sweep", _graph_time(fused(rk), args.steps, args.warmup, stream), rk)
+        del sets, w16
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,11 +302,17 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before timing, copy 256 MiB device-to-device 4 times (a kernel of known "
                          "traffic for scaling hardware counters)")
+    ap.add_argument("--compare", action="store_true",
+                    help="instead of the benchmark line: fused vs unfused vs residual-only vs dense fp16, "
+                         "and a rank sweep, one JSON line each")
+    ap.add_argument("--compare-configs", default="", help="comma-separated workloads for --compare")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the layer is benchmarked on one "
                                    "MI355X; run with --gpus 1"}))
         sys.exit(2)
+    if args.compare:
+        return compare(args)
 
     import numpy as np
     import torch

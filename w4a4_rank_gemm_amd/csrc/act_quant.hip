@@ -302,8 +302,10 @@ __global__ __launch_bounds__(kActThreads) void act_kernel(ActArgs a, ActDev p) {
     }
 }
 
-// T[row][c] = sum over slices s (in slice order) of partials[s][row][c]. Loads are
-// issued eight slices at a time before any is added.
+// T[row][c] = sum over slices s (in slice order) of partials[s][row][c]. The data is
+// small and the kernel latency-bound, so every load of a thread is issued before any
+// is added (KS_MAX slices in flight; loads past ks re-read slice 0 and are not added).
+template <int KS_MAX>
 __global__ __launch_bounds__(256) void t_reduce_kernel(const float *partials, int64_t b, int64_t rows_pad,
                                                        int r, int ks, float *t) {
     const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 index into T
@@ -311,16 +313,13 @@ __global__ __launch_bounds__(256) void t_reduce_kernel(const float *partials, in
     if (i4 >= n4) return;
     const int64_t stride = rows_pad * r;
     const float *src = partials + i4 * 4;
-    v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < ks; s0 += 8) {
-        v4f v[8];
+    v4f v[KS_MAX];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (s0 + u < ks) v[u] = *reinterpret_cast<const v4f *>(src + (s0 + u) * stride);
+    for (int u = 0; u < KS_MAX; ++u) v[u] = *reinterpret_cast<const v4f *>(src + (u < ks ? u : 0) * stride);
+    v4f sum = v[0];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (s0 + u < ks) sum += v[u];
-    }
+    for (int u = 1; u < KS_MAX; ++u)
+        if (u < ks) sum += v[u];
     *reinterpret_cast<v4f *>(t + i4 * 4) = sum;
 }
 
@@ -337,13 +336,14 @@ ActPlan plan_act(int64_t b, int64_t m, int64_t r) {
     if (b == 0) return pl;
     if (b > 128) {
         // many tokens: 128-row tiles x all ranks; K slices (steps of 32, at least 512
-        // long) until about 256 CTAs
+        // long, at most 32 of them) until about 256 CTAs
         pl.mode = 0;
         pl.row_tile = 128;
         pl.row_tiles = (int)((b + 127) / 128);
         int64_t ks = 1;
         if (r > 0)
-            while ((int64_t)pl.row_tiles * ks < 256 && m / (ks * 2) >= 512 && m % (ks * 2 * 32) == 0) ks *= 2;
+            while ((int64_t)pl.row_tiles * ks < 256 && ks < 32 && m / (ks * 2) >= 512 && m % (ks * 2 * 32) == 0)
+                ks *= 2;
         pl.ks = (int)ks;
     } else {
         // few tokens: every token x one 16-rank tile x one K slice per CTA, slices of
@@ -421,8 +421,15 @@ hipError_t launch_act(const ActArgs &a, const ActPlan &pl, hipStream_t stream) {
     if (e != hipSuccess || a.r == 0 || pl.ks == 1 || a.keep_partials) return e;
     const int64_t n4 = a.b * a.r / 4;
     const int64_t rows_pad = pl.mode == 0 ? (int64_t)pl.row_tiles * 128 : (int64_t)pl.fm * 16;
-    hipLaunchKernelGGL(t_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a.partials, a.b,
-                       rows_pad, a.r, pl.ks, a.t);
+    const dim3 rgrid((unsigned)((n4 + 255) / 256));
+    if (pl.ks <= 8)
+        hipLaunchKernelGGL(t_reduce_kernel<8>, rgrid, dim3(256), 0, stream, a.partials, a.b, rows_pad, a.r, pl.ks, a.t);
+    else if (pl.ks <= 16)
+        hipLaunchKernelGGL(t_reduce_kernel<16>, rgrid, dim3(256), 0, stream, a.partials, a.b, rows_pad, a.r, pl.ks, a.t);
+    else if (pl.ks <= 32)
+        hipLaunchKernelGGL(t_reduce_kernel<32>, rgrid, dim3(256), 0, stream, a.partials, a.b, rows_pad, a.r, pl.ks, a.t);
+    else
+        return hipErrorInvalidValue;  // plan_act keeps ks <= 32
     return hipGetLastError();
 }
 

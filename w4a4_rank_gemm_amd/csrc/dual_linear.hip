@@ -265,17 +265,24 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
                         }
                     y = mfma_f16(l2f[s], live ? f32x8_to_h8(t0, t1) : v8h{}, y);
                 }
-            } else {
+            } else if constexpr (RS > 0) {
+                // every rank step's L2^T and T pieces are loaded before the first is used
                 const int64_t chr = ch0 + fn_e * 16 + li, tokr = fm_e * 16 + li;
                 const uint16_t *l2row = a.l2t + (chr < a.n ? chr : a.n - 1) * a.r;
                 const float *trow = a.t + (tokr < a.b ? tokr : a.b - 1) * a.r;
-                for (int k0 = 0; k0 < a.r; k0 += 32) {
-                    const int rank = k0 + g * 8;
-                    const bool live = rank < a.r;
-                    const int rk = live ? rank : 0;
-                    const float4 *tp = reinterpret_cast<const float4 *>(trow + rk);
-                    y = mfma_f16(load_h8(l2row + rk), live ? f32x8_to_h8(tp[0], tp[1]) : v8h{}, y);
+                v8h la[RS];
+                float4 ta[RS], tb[RS];
+#pragma unroll
+                for (int s = 0; s < RS; ++s) {
+                    const int rank = s * 32 + g * 8;
+                    const int rk = rank < a.r ? rank : 0;
+                    la[s] = load_h8(l2row + rk);
+                    ta[s] = *reinterpret_cast<const float4 *>(trow + rk);
+                    tb[s] = *reinterpret_cast<const float4 *>(trow + rk + 4);
                 }
+#pragma unroll
+                for (int s = 0; s < RS; ++s)
+                    y = mfma_f16(la[s], s * 32 + g * 8 < a.r ? f32x8_to_h8(ta[s], tb[s]) : v8h{}, y);
             }
             if (store) {
                 v4h o;
