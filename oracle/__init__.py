@@ -68,6 +68,11 @@ def _load():
         lib.orc_dual_linear_grouped.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
         lib.orc_dual_linear_grouped_sampled.restype = ctypes.c_int
         lib.orc_dual_linear_grouped_sampled.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P]
+        lib.orc_quantize_act_a8.argtypes = [_P, _I, _I, _P, _P]
+        lib.orc_dual_linear_a8.restype = ctypes.c_int
+        lib.orc_dual_linear_a8.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
+        lib.orc_dual_linear_a8_sampled.restype = ctypes.c_int
+        lib.orc_dual_linear_a8_sampled.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P]
         lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -353,6 +358,57 @@ def dual_linear_grouped_sampled(x, w_res, l1t, l2t, g, rows, cols):
     if rc:
         raise MemoryError("oracle allocation failed")
     return y
+
+
+def quantize_act_a8(x):
+    """8-bit activation quantizer (q_max = 127): (codes int8 [b][m], s_X f32 [b])."""
+    xb = _h(x)
+    b, m = xb.shape
+    q = np.empty((b, m), np.int8)
+    s = np.empty(b, np.float32)
+    _load().orc_quantize_act_a8(_p(xb), b, m, _p(q), _p(s))
+    return q, s
+
+
+def dual_linear_a8(x, w_res, l1t, l2t):
+    """The W4A8 layer: dict qx (int8 [b][m]), sx, qw_packed, sw, acc (int64), y (f64)."""
+    xb = _h(x)
+    w = _c(w_res, np.float32)
+    b, m = xb.shape
+    n = w.shape[0]
+    l1 = _h(l1t) if l1t is not None else np.zeros((0, m), np.uint16)
+    l2 = _h(l2t) if l2t is not None else np.zeros((n, 0), np.uint16)
+    r = l1.shape[0]
+    out = {"qx": np.empty((b, m), np.int8), "sx": np.empty(b, np.float32),
+           "qw_packed": np.empty((n, m // 2), np.uint8), "sw": np.empty(n, np.float32),
+           "acc": np.empty((b, n), np.int64), "y": np.empty((b, n), np.float64)}
+    rc = _load().orc_dual_linear_a8(_p(xb), _p(w), _p(l1), _p(l2), b, m, n, r, _p(out["qx"]), _p(out["sx"]),
+                                    _p(out["qw_packed"]), _p(out["sw"]), _p(out["acc"]), _p(out["y"]))
+    if rc:
+        raise MemoryError("oracle allocation failed")
+    return out
+
+
+def dual_linear_a8_sampled(x, w_res, l1t, l2t, rows, cols):
+    """The W4A8 layer at the positions (rows[p], cols[p]): (acc, y)."""
+    xb = _h(x)
+    w = _c(w_res, np.float32)
+    b, m = xb.shape
+    n = w.shape[0]
+    l1 = _h(l1t) if l1t is not None else np.zeros((0, m), np.uint16)
+    l2 = _h(l2t) if l2t is not None else np.zeros((n, 0), np.uint16)
+    r = l1.shape[0]
+    rows = _c(rows, np.int64)
+    cols = _c(cols, np.int64)
+    assert rows.shape == cols.shape and rows.ndim == 1
+    assert ((0 <= rows) & (rows < b)).all() and ((0 <= cols) & (cols < n)).all()
+    acc = np.empty(rows.shape[0], np.int64)
+    y = np.empty(rows.shape[0], np.float64)
+    rc = _load().orc_dual_linear_a8_sampled(_p(xb), _p(w), _p(l1), _p(l2), b, m, n, r, _p(rows), _p(cols),
+                                            rows.shape[0], _p(acc), _p(y))
+    if rc:
+        raise MemoryError("oracle allocation failed")
+    return acc, y
 
 
 def unpack_codes(packed):

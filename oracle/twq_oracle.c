@@ -37,7 +37,9 @@
  * identity that exactly representable factors reproduce the fp16 branch; for
  * group-wise scales a hand-worked two-group layer, the identities g = m (one
  * group: the per-token layer) and grouped rows = per-row quantization of the
- * rows cut into groups, and brute force with exact rationals.
+ * rows cut into groups, and brute force with exact rationals; for W4A8 a
+ * hand-worked layer with ties at q_max = 127, the rational model at 8 bits, the
+ * largest code reached for every fp16 amax, and a library int64 matmul.
  * The pages' own kernel numerics (its s_H granularity in particular) print no
  * example and stay a reading, not a pin.
  */
@@ -65,8 +67,9 @@ double orc_half_to_double(uint16_t h)
     return sign ? -v : v;
 }
 
-/* eq. (1) on one vector held in binary32: s = max|v| / q_max, q = round(v / s). */
-static void quantize_vector(const float *v, int64_t len, int8_t *q, float *s_out)
+/* eq. (1) on one vector held in binary32 with q_max = 2^(k-1) - 1 for k bits:
+ * s = max|v| / q_max, q = round(v / s). */
+static void quantize_vector_q(const float *v, int64_t len, int q_max, int8_t *q, float *s_out)
 {
     float amax = 0.0f;
     for (int64_t k = 0; k < len; k++) {
@@ -74,7 +77,7 @@ static void quantize_vector(const float *v, int64_t len, int8_t *q, float *s_out
         if (a > amax)
             amax = a;
     }
-    float s = amax / (float)Q_MAX;
+    float s = amax / (float)q_max;
     *s_out = s;
     for (int64_t k = 0; k < len; k++) {
         if (amax == 0.0f) {
@@ -83,12 +86,18 @@ static void quantize_vector(const float *v, int64_t len, int8_t *q, float *s_out
         }
         float ratio = v[k] / s;      /* one binary32 division */
         float r = rintf(ratio);      /* round half to even */
-        if (r > Q_MAX)
-            r = Q_MAX;
-        if (r < -Q_MAX)
-            r = -Q_MAX;
+        if (r > q_max)
+            r = (float)q_max;
+        if (r < -q_max)
+            r = (float)-q_max;
         q[k] = (int8_t)r;
     }
+}
+
+/* the 4-bit case of eq. (1) */
+static void quantize_vector(const float *v, int64_t len, int8_t *q, float *s_out)
+{
+    quantize_vector_q(v, len, Q_MAX, q, s_out);
 }
 
 /* two codes per byte: element 2t in the low nibble, element 2t+1 in the high nibble */
@@ -418,6 +427,108 @@ int orc_dual_linear_lr4_sampled(const uint16_t *x, const float *w_res, const uin
         free(xr); free(qx); free(qw); free(qh);
     }
     free(ql1); free(ql2); free(sl1); free(sl2); free(c);
+    return fail;
+}
+
+/* ---- W4A8 (TwinQuant page 1, section 5.1: WxAy names x-bit weights and y-bit
+ * activations; W4A8 results in page 1, section 5.2 and page 2, section A.3) ----
+ *
+ * The residual weight stays 4-bit (q_max = 7); the activations are quantized per
+ * token with eq. (1) at k = 8 bits, q_max = 2^7 - 1 = 127, codes stored one int8 per
+ * element. Everything else is the layer above:
+ *   Y[i][j] = s_X[i] s_W[j] sum_k Q_X[i][k] Q_W[j][k] + LR[i][j]. */
+#define Q_MAX_A8 127
+
+/* X fp16 [b][m] -> codes int8 [b][m], s_X f32 [b] */
+void orc_quantize_act_a8(const uint16_t *x, int64_t b, int64_t m, int8_t *qx, float *sx)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < b; i++) {
+        float *row = (float *)malloc(sizeof(float) * (size_t)m);
+        for (int64_t k = 0; k < m; k++)
+            row[k] = (float)orc_half_to_double(x[i * m + k]);
+        quantize_vector_q(row, m, Q_MAX_A8, qx + i * m, sx + i);
+        free(row);
+    }
+}
+
+/* The W4A8 layer, binary64. Outputs other than y may be NULL. */
+int orc_dual_linear_a8(const uint16_t *x, const float *w_res, const uint16_t *l1t,
+                       const uint16_t *l2t, int64_t b, int64_t m, int64_t n, int64_t r,
+                       int8_t *qx_out, float *sx, uint8_t *qw_packed, float *sw,
+                       int64_t *acc_out, double *y)
+{
+    int8_t *qx = (int8_t *)malloc((size_t)(b * m));
+    int8_t *qw = (int8_t *)malloc((size_t)(n * m));
+    float *sx_l = (float *)malloc(sizeof(float) * (size_t)b);
+    float *sw_l = (float *)malloc(sizeof(float) * (size_t)n);
+    int64_t *acc = (int64_t *)malloc(sizeof(int64_t) * (size_t)(b * n));
+    double *t = (double *)malloc(sizeof(double) * (size_t)(b * (r > 0 ? r : 1)));
+    double *lr = (double *)malloc(sizeof(double) * (size_t)(b * n));
+    if (!qx || !qw || !sx_l || !sw_l || !acc || !t || !lr)
+        return 1;
+    orc_quantize_act_a8(x, b, m, qx, sx_l);
+    orc_quantize_weight(w_res, n, m, qw, qw_packed, sw_l);
+    orc_residual_acc(qx, qw, b, m, n, acc);
+    if (r > 0) {
+        orc_lowrank_t(x, l1t, b, m, r, t);
+        orc_lowrank_out(t, l2t, b, n, r, lr);
+    } else {
+        memset(lr, 0, sizeof(double) * (size_t)(b * n));
+    }
+    for (int64_t i = 0; i < b; i++)
+        for (int64_t j = 0; j < n; j++)
+            y[i * n + j] = (double)sx_l[i] * (double)sw_l[j] * (double)acc[i * n + j] + lr[i * n + j];
+    if (qx_out)
+        memcpy(qx_out, qx, (size_t)(b * m));
+    if (sx)
+        memcpy(sx, sx_l, sizeof(float) * (size_t)b);
+    if (sw)
+        memcpy(sw, sw_l, sizeof(float) * (size_t)n);
+    if (acc_out)
+        memcpy(acc_out, acc, sizeof(int64_t) * (size_t)(b * n));
+    free(qx); free(qw); free(sx_l); free(sw_l); free(acc); free(t); free(lr);
+    return 0;
+}
+
+/* The W4A8 layer at sampled positions: acc and Y at (rows[p], cols[p]). */
+int orc_dual_linear_a8_sampled(const uint16_t *x, const float *w_res, const uint16_t *l1t,
+                               const uint16_t *l2t, int64_t b, int64_t m, int64_t n, int64_t r,
+                               const int64_t *rows, const int64_t *cols, int64_t count,
+                               int64_t *acc_out, double *y_out)
+{
+    (void)b;
+    (void)n;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < count; p++) {
+        int64_t i = rows[p], j = cols[p];
+        float *xr = (float *)malloc(sizeof(float) * (size_t)m);
+        int8_t *qx = (int8_t *)malloc((size_t)m);
+        int8_t *qw = (int8_t *)malloc((size_t)m);
+        if (!xr || !qx || !qw) {
+            fail = 1;
+            continue;
+        }
+        float sxi, swj;
+        for (int64_t k = 0; k < m; k++)
+            xr[k] = (float)orc_half_to_double(x[i * m + k]);
+        quantize_vector_q(xr, m, Q_MAX_A8, qx, &sxi);
+        quantize_vector(w_res + j * m, m, qw, &swj);
+        int64_t acc = 0;
+        for (int64_t k = 0; k < m; k++)
+            acc += (int64_t)qx[k] * (int64_t)qw[k];
+        double lr = 0.0;
+        for (int64_t u = 0; u < r; u++) {
+            double tu = 0.0;
+            for (int64_t k = 0; k < m; k++)
+                tu += orc_half_to_double(x[i * m + k]) * orc_half_to_double(l1t[u * m + k]);
+            lr += tu * orc_half_to_double(l2t[j * r + u]);
+        }
+        acc_out[p] = acc;
+        y_out[p] = (double)sxi * (double)swj * (double)acc + lr;
+        free(xr); free(qx); free(qw);
+    }
     return fail;
 }
 

@@ -506,3 +506,79 @@ def test_grouped_sampled_matches_full(oracle_lib):
     cols = rng.integers(0, 40, 50)
     y = oracle_lib.dual_linear_grouped_sampled(d["x"], d["w_res"], d["l1t"], d["l2t"], 128, rows, cols)
     assert (y == full["y"][rows, cols]).all()
+
+
+# ---------------------------------------------------------------- W4A8 (8-bit activations, q_max = 127)
+
+def test_a8_hand_worked(oracle_lib):
+    with open(os.path.join(GOLDEN, "w4a8_layer.json")) as f:
+        gd = json.load(f)
+    x = np.array(gd["x"], np.float16)
+    out = oracle_lib.dual_linear_a8(x, np.array(gd["w_res"], np.float32), None, None)
+    assert out["qx"].tolist() == gd["qx"] and out["sx"].astype(np.float64).tolist() == gd["sx"]
+    assert oracle_lib.unpack_codes(out["qw_packed"]).tolist() == gd["qw"]
+    assert out["sw"].astype(np.float64).tolist() == gd["sw"]
+    assert out["acc"].tolist() == gd["acc"] and out["y"].tolist() == gd["y"]
+
+
+def test_a8_rational_bruteforce(oracle_lib):
+    """Codes and scales of the 8-bit quantizer from exact rationals (binary32 roundings
+    decided by the rational model), the integer sum by brute force, Y exactly."""
+    rng = synth.rng_for(50)
+    b, m, n, r = 4, 24, 6, 3
+    x = (rng.standard_normal((b, m)) * np.array([1.0] * 20 + [40.0] * 4)).astype(np.float16)
+    x[2] = 0
+    w = (rng.standard_t(3, size=(n, m)) * 0.02).astype(np.float32)
+    l1t = rng.standard_normal((r, m)).astype(np.float16)
+    l2t = rng.standard_normal((n, r)).astype(np.float16)
+    out = oracle_lib.dual_linear_a8(x, w, l1t, l2t)
+    qw = oracle_lib.unpack_codes(out["qw_packed"])
+    xf = [[F(float(v)) for v in row] for row in x]
+    for i in range(b):
+        s, q = ratmodel.quantize(xf[i], q_max=127)
+        assert F(float(out["sx"][i])) == s and out["qx"][i].tolist() == q
+    l1 = [[F(float(v)) for v in row] for row in l1t]
+    l2 = [[F(float(v)) for v in row] for row in l2t]
+    for i in range(b):
+        t = [sum(xf[i][k] * l1[u][k] for k in range(m)) for u in range(r)]
+        for j in range(n):
+            acc = sum(int(out["qx"][i, k]) * int(qw[j, k]) for k in range(m))
+            assert out["acc"][i, j] == acc
+            y = F(float(out["sx"][i])) * F(float(out["sw"][j])) * acc + sum(t[u] * l2[j][u] for u in range(r))
+            assert abs(float(y) - out["y"][i, j]) <= 1e-12 * max(1.0, abs(float(y)))
+
+
+def test_a8_max_code_is_127_for_every_fp16_amax(oracle_lib):
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)  # every positive finite fp16
+    amax = bits.view(np.float16)
+    x = np.stack([amax, -amax, np.zeros_like(amax)], axis=1)
+    q, s = oracle_lib.quantize_act_a8(x)
+    assert (q[:, 0] == 127).all() and (q[:, 1] == -127).all() and (q[:, 2] == 0).all()
+    assert (s == (amax.astype(np.float32) / np.float32(127))).all()
+
+
+def test_a8_invariants(oracle_lib):
+    rng = synth.rng_for(51)
+    x = rng.standard_normal((32, 64)).astype(np.float16)
+    q, s = oracle_lib.quantize_act_a8(x)
+    qn, sn = oracle_lib.quantize_act_a8(-x)
+    assert (qn == -q).all() and (sn == s).all()
+    for e in (-3, 4):
+        q2, s2 = oracle_lib.quantize_act_a8((x.astype(np.float32) * 2.0 ** e).astype(np.float16))
+        assert (q2 == q).all() and (s2 == s * np.float32(2.0 ** e)).all()
+    # within half a step: |x - s q| <= s / 2
+    assert (np.abs(x.astype(np.float64) - s[:, None].astype(np.float64) * q) <= s[:, None] / 2 * (1 + 1e-6)).all()
+
+
+def test_a8_library_matmul_and_sampled(oracle_lib):
+    d = synth.make_random(9, 256, 40, 16, seed=52)
+    out = oracle_lib.dual_linear_a8(d["x"], d["w_res"], d["l1t"], d["l2t"])
+    qw = oracle_lib.unpack_codes(out["qw_packed"]).astype(np.int64)
+    assert (out["acc"] == out["qx"].astype(np.int64) @ qw.T).all()
+    lr = oracle_lib.lowrank_out(oracle_lib.lowrank_t(d["x"], d["l1t"]), d["l2t"])
+    ref = out["sx"].astype(np.float64)[:, None] * out["sw"].astype(np.float64)[None, :] * out["acc"] + lr
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-15, atol=1e-12)
+    rng = synth.rng_for(53)
+    rows, cols = rng.integers(0, 9, 40), rng.integers(0, 40, 40)
+    acc, y = oracle_lib.dual_linear_a8_sampled(d["x"], d["w_res"], d["l1t"], d["l2t"], rows, cols)
+    assert (acc == out["acc"][rows, cols]).all() and (y == out["y"][rows, cols]).all()
