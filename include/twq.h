@@ -185,6 +185,32 @@ twq_status twq_linear_grouped(const void *x, const void *qw, const float *sw, co
                               int64_t g, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ---- W4A8 (TwinQuant page 1, section 5.1: WxAy names x-bit weights and y-bit
+ * activations; W4A8 results in page 1, section 5.2 and page 2, section A.3) ----
+ *
+ * The activations are quantized per token by eq. (1) with k = 8 bits, q_max = 127,
+ * and stored one int8 code per element, K-contiguous:
+ *   qx    i8  [b][m]      codes Q_X in [-127, 127]
+ *   sx    f32 [b]         s_X = max_k |x[i][k]| / 127
+ * The residual weight is the 4-bit Q_W, s_W of twq_pack_weight. The integer sum is
+ * exact (int32; |acc| <= 889 m). Everything else (T, the low-rank branch, the
+ * workspace rules, the errors) is as for the 4-bit entry points of the same name.
+ */
+twq_status twq_quantize_act_a8(const void *x, int64_t b, int64_t m, void *qx, float *sx,
+                               const void *l1t, int64_t r, float *t, void *workspace,
+                               size_t workspace_bytes, void *stream);
+twq_status twq_dual_linear_a8(const void *qx, const float *sx, const void *qw, const float *sw,
+                              const float *t, const void *l2t, int64_t r, void *y, int64_t b,
+                              int64_t m, int64_t n, void *stream);
+size_t twq_linear_a8_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r);
+twq_status twq_linear_a8(const void *x, const void *qw, const float *sw, const void *l1t,
+                         const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n,
+                         void *workspace, size_t workspace_bytes, void *stream);
+/* Test export: the W4A8 main loop storing the exact int32 acc[i][j] = sum_k Q_X[i][k] Q_W[j][k]. */
+twq_status twq_debug_residual_acc_a8(const void *qx, const void *qw, int32_t *acc, int64_t b,
+                                     int64_t m, int64_t n, void *stream);
+
+/*
  * ---- int4 low-rank variant (TwinQuant page 1, section 4.3) ----
  *
  * Both low-rank factors in 4 bits: the first low-rank GEMM gives INT32 H = Q_X Q_L1,

@@ -147,3 +147,19 @@ def test_grouped_validation():
     assert grouped >= per_token + 16 * 4 * (4096 // 128 - 1) - 255
     assert L.twq_linear_grouped(A, A, A, A, A, 32, A, 16, 4096, 4096, 128, A, grouped - 1, None) == WORKSPACE
     assert L.twq_linear_grouped(None, None, None, None, None, 32, None, 0, 4096, 4096, 128, None, 0, None) == OK
+
+
+def test_a8_validation():
+    L = twq.lib()
+    assert L.twq_quantize_act_a8(A, 16, 4000, A, A, None, 0, None, None, 0, None) == SHAPE
+    assert L.twq_quantize_act_a8(None, 16, 4096, A, A, None, 0, None, None, 0, None) == NULL
+    assert L.twq_quantize_act_a8(A, 0, 4096, None, None, None, 0, None, None, 0, None) == OK
+    assert L.twq_dual_linear_a8(A, A, A, A, None, None, 32, A, 16, 4096, 64, None) == NULL
+    assert L.twq_dual_linear_a8(A, A, MIS, A, None, None, 0, A, 16, 4096, 64, None) == ALIGN
+    assert L.twq_dual_linear_a8(A, A, A, A, None, None, 0, A, 16, 4096, 40, None) == SHAPE
+    assert L.twq_debug_residual_acc_a8(A, A, None, 16, 4096, 64, None) == NULL
+    need4 = L.twq_linear_workspace_bytes(16, 4096, 4096, 32)
+    need8 = L.twq_linear_a8_workspace_bytes(16, 4096, 4096, 32)
+    assert need8 >= need4 + 16 * 4096 // 2 - 255  # one byte per activation code instead of half a byte
+    assert L.twq_linear_a8(A, A, A, A, A, 32, A, 16, 4096, 4096, A, need8 - 1, None) == WORKSPACE
+    assert L.twq_linear_a8(None, None, None, None, None, 32, None, 0, 4096, 4096, None, 0, None) == OK

@@ -29,7 +29,9 @@ EXPORTS = ("twq_status_string", "twq_last_error_string", "twq_version",
            "twq_quantize_act_workspace_bytes", "twq_quantize_act", "twq_pack_weight",
            "twq_dual_linear", "twq_debug_residual_acc", "twq_linear_workspace_bytes",
            "twq_linear", "twq_quantize_act_grouped", "twq_pack_weight_grouped", "twq_dual_linear_grouped",
-           "twq_linear_grouped_workspace_bytes", "twq_linear_grouped", "twq_pack_lowrank_int4",
+           "twq_linear_grouped_workspace_bytes", "twq_linear_grouped", "twq_quantize_act_a8",
+           "twq_dual_linear_a8", "twq_linear_a8_workspace_bytes", "twq_linear_a8", "twq_debug_residual_acc_a8",
+           "twq_pack_lowrank_int4",
            "twq_lowrank_requant", "twq_dual_linear_lr4")
 
 GROUP = 128  # group size of the group-wise entry points
@@ -88,6 +90,16 @@ def lib() -> ctypes.CDLL:
                 L.twq_linear_grouped_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
                 L.twq_linear_grouped.restype = ctypes.c_int
                 L.twq_linear_grouped.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _P, _S, _P]
+                L.twq_quantize_act_a8.restype = ctypes.c_int
+                L.twq_quantize_act_a8.argtypes = [_P, _I, _I, _P, _P, _P, _I, _P, _P, _S, _P]
+                L.twq_dual_linear_a8.restype = ctypes.c_int
+                L.twq_dual_linear_a8.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P]
+                L.twq_linear_a8_workspace_bytes.restype = _S
+                L.twq_linear_a8_workspace_bytes.argtypes = [_I, _I, _I, _I]
+                L.twq_linear_a8.restype = ctypes.c_int
+                L.twq_linear_a8.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _S, _P]
+                L.twq_debug_residual_acc_a8.restype = ctypes.c_int
+                L.twq_debug_residual_acc_a8.argtypes = [_P, _P, _P, _I, _I, _I, _P]
                 L.twq_pack_lowrank_int4.restype = ctypes.c_int
                 L.twq_pack_lowrank_int4.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]
                 L.twq_lowrank_requant.restype = ctypes.c_int
@@ -326,6 +338,96 @@ def linear_grouped(x: torch.Tensor, qw, sw, l1t=None, l2t=None, out: torch.Tenso
     _check(L.twq_linear_grouped(_ptr(x), _ptr(qw), _ptr(sw), _ptr(l1t), _ptr(l2t), r, _ptr(y), b, m, n, g,
                                 _ptr(ws), wsb, _stream(dev)), "twq_linear_grouped")
     return y
+
+
+# ---- W4A8: 8-bit activation codes (int8 [b][m]), 4-bit residual weight ----
+
+def quantize_act_a8(x: torch.Tensor, l1t: torch.Tensor | None = None):
+    """X fp16 [b][m] -> (Q_X int8 [b][m], s_X f32 [b], T f32 [b][r] or None)."""
+    _need(x, "x", torch.float16, 2)
+    b, m = x.shape
+    r = 0
+    if l1t is not None:
+        _need(l1t, "l1t", torch.float16, 2)
+        r = l1t.shape[0]
+        if l1t.shape[1] != m or l1t.device != x.device:
+            raise ValueError("l1t must be [r][m] on x's device")
+    dev = x.device
+    qx = torch.empty((b, m), dtype=torch.int8, device=dev)
+    sx = torch.empty((b,), dtype=torch.float32, device=dev)
+    t = torch.empty((b, r), dtype=torch.float32, device=dev) if r else None
+    L = lib()
+    ws, wsb = _workspace(dev, L.twq_quantize_act_workspace_bytes(b, m, r))
+    _check(L.twq_quantize_act_a8(_ptr(x), b, m, _ptr(qx), _ptr(sx), _ptr(l1t), r, _ptr(t),
+                                 _ptr(ws), wsb, _stream(dev)), "twq_quantize_act_a8")
+    return qx, sx, t
+
+
+def dual_linear_a8(qx, sx, qw, sw, t=None, l2t=None, out: torch.Tensor | None = None):
+    """The fused W4A8 layer: Y fp16 [b][n]."""
+    _need(qx, "qx", torch.int8, 2)
+    _need(qw, "qw", torch.uint8, 2)
+    _need(sx, "sx", torch.float32, 1)
+    _need(sw, "sw", torch.float32, 1)
+    b, m = qx.shape
+    n = qw.shape[0]
+    if qw.shape[1] != m // 2 or sx.shape[0] != b or sw.shape[0] != n:
+        raise ValueError("inconsistent shapes of qx/sx/qw/sw")
+    r = 0
+    if l2t is not None or t is not None:
+        _need(t, "t", torch.float32, 2)
+        _need(l2t, "l2t", torch.float16, 2)
+        r = l2t.shape[1]
+        if t.shape != (b, r) or l2t.shape[0] != n:
+            raise ValueError("t must be [b][r] and l2t [n][r]")
+    dev = qx.device
+    y = out if out is not None else torch.empty((b, n), dtype=torch.float16, device=dev)
+    _need(y, "out", torch.float16, 2)
+    if y.shape != (b, n):
+        raise ValueError("out must be [b][n]")
+    _check(lib().twq_dual_linear_a8(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), _ptr(t), _ptr(l2t), r,
+                                    _ptr(y), b, m, n, _stream(dev)), "twq_dual_linear_a8")
+    return y
+
+
+def linear_a8(x: torch.Tensor, qw, sw, l1t=None, l2t=None, out: torch.Tensor | None = None):
+    """The whole W4A8 layer in one call (twq_linear_a8): Y fp16 [b][n]."""
+    _need(x, "x", torch.float16, 2)
+    _need(qw, "qw", torch.uint8, 2)
+    _need(sw, "sw", torch.float32, 1)
+    b, m = x.shape
+    n = qw.shape[0]
+    if qw.shape[1] != m // 2 or sw.shape[0] != n:
+        raise ValueError("inconsistent shapes of x/qw/sw")
+    r = 0
+    if l1t is not None or l2t is not None:
+        _need(l1t, "l1t", torch.float16, 2)
+        _need(l2t, "l2t", torch.float16, 2)
+        r = l1t.shape[0]
+        if l1t.shape[1] != m or l2t.shape != (n, r):
+            raise ValueError("l1t must be [r][m] and l2t [n][r]")
+    dev = x.device
+    y = out if out is not None else torch.empty((b, n), dtype=torch.float16, device=dev)
+    _need(y, "out", torch.float16, 2)
+    if y.shape != (b, n):
+        raise ValueError("out must be [b][n]")
+    L = lib()
+    ws, wsb = _workspace(dev, L.twq_linear_a8_workspace_bytes(b, m, n, r))
+    _check(L.twq_linear_a8(_ptr(x), _ptr(qw), _ptr(sw), _ptr(l1t), _ptr(l2t), r, _ptr(y), b, m, n,
+                           _ptr(ws), wsb, _stream(dev)), "twq_linear_a8")
+    return y
+
+
+def debug_residual_acc_a8(qx, qw):
+    """int32 [b][n] = Q_X (8-bit) . Q_W^T (4-bit) computed by the W4A8 main loop."""
+    _need(qx, "qx", torch.int8, 2)
+    _need(qw, "qw", torch.uint8, 2)
+    b, m = qx.shape
+    n = qw.shape[0]
+    acc = torch.empty((b, n), dtype=torch.int32, device=qx.device)
+    _check(lib().twq_debug_residual_acc_a8(_ptr(qx), _ptr(qw), _ptr(acc), b, m, n, _stream(qx.device)),
+           "twq_debug_residual_acc_a8")
+    return acc
 
 
 def debug_residual_acc(qx, qw):

@@ -51,10 +51,25 @@ __device__ __forceinline__ uint32_t quant8(const uint4 c, float s, float inv) {
     return pack8(q);
 }
 
+// Eight 8-bit codes (q_max = 127) of one 16-byte chunk of fp16, one byte each in order.
+__device__ __forceinline__ uint2 quant8_a8(const uint4 c, float s, float inv) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (uint32_t)quant_code8_fast(half_bits_to_float(w[e] & 0xFFFFu), s, inv) & 0xFFu;
+        const uint32_t hi = (uint32_t)quant_code8_fast(half_bits_to_float(w[e] >> 16), s, inv) & 0xFFu;
+        out[e / 2] |= (lo | (hi << 8)) << (16 * (e % 2));
+    }
+    return make_uint2(out[0], out[1]);
+}
+
 // Slice sl (of nsl) of one token row, by one CTA of 256 threads: amax is taken over
 // the whole row (every slice reads it; only the first reads it from HBM), the codes
 // are written for the slice's chunks only. Spreading a short row over several
-// CTAs spreads its divisions over several compute units.
+// CTAs spreads its divisions over several compute units. A8: 8-bit codes
+// (q_max = 127), one byte each.
+template <bool A8>
 __device__ void quantize_row(const ActArgs &a, int64_t i, int sl, int nsl, uint32_t *red) {
     const int tid = threadIdx.x;
     const int64_t nch = a.m / 8;  // 16-byte chunks of 8 fp16
@@ -81,17 +96,24 @@ __device__ void quantize_row(const ActArgs &a, int64_t i, int sl, int nsl, uint3
 #pragma unroll
     for (int w = 1; w < kActThreads / kWave; ++w) mx = mx > red[w] ? mx : red[w];
     const float amax = half_bits_to_float(mx);
-    const float s = amax / kQMax;  // correctly rounded binary32 division
-    const float inv = 1.0f / s;    // only used when amax > 0
+    const float s = amax / (A8 ? kQMax8 : kQMax);  // correctly rounded binary32 division
+    const float inv = 1.0f / s;                     // only used when amax > 0
     if (tid == 0 && sl == 0) a.sx[i] = s;
+    uint2 *qr8 = reinterpret_cast<uint2 *>(a.qx + i * a.m);
+    auto put = [&](int64_t c, const uint4 chunk) {
+        if constexpr (A8)
+            qr8[c] = amax == 0.0f ? make_uint2(0u, 0u) : quant8_a8(chunk, s, inv);
+        else
+            qr[c] = amax == 0.0f ? 0u : quant8(chunk, s, inv);
+    };
     if (cached) {
 #pragma unroll
         for (int j = 0; j < kActMaxJ; ++j) {
             const int64_t c = tid + (int64_t)j * kActThreads;
-            if (c >= c_lo && c < c_hi) qr[c] = amax == 0.0f ? 0u : quant8(v[j], s, inv);
+            if (c >= c_lo && c < c_hi) put(c, v[j]);
         }
     } else {
-        for (int64_t c = c_lo + tid; c < c_hi; c += kActThreads) qr[c] = amax == 0.0f ? 0u : quant8(xr[c], s, inv);
+        for (int64_t c = c_lo + tid; c < c_hi; c += kActThreads) put(c, xr[c]);
     }
 }
 
@@ -297,8 +319,10 @@ __global__ __launch_bounds__(kActThreads) void act_kernel(ActArgs a, ActDev p) {
         const int64_t q = bid - p.n_t_ctas;
         if (a.group)
             quantize_row_grouped(a, q / p.nsl, (int)(q % p.nsl), p.nsl);
+        else if (a.a8)
+            quantize_row<true>(a, q / p.nsl, (int)(q % p.nsl), p.nsl, red);
         else
-            quantize_row(a, q / p.nsl, (int)(q % p.nsl), p.nsl, red);
+            quantize_row<false>(a, q / p.nsl, (int)(q % p.nsl), p.nsl, red);
     }
 }
 

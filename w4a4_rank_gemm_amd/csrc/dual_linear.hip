@@ -64,9 +64,17 @@ constexpr int kMaxTSlices = 16;
 // packed row is one group, so each piece's integer sum is formed from zero and added to
 // an fp32 accumulator times s_X[group][token] s_W[group][channel], loaded beside the
 // piece; the waves' fp32 partial sums are added through LDS in wave order.
-template <int FN, int FM, int U, int RS, bool STORE_ACC, int TK = 1, int NW = 4, bool GRP = false>
+//
+// W4A8 (A8): the token rows hold one int8 code per element, so a 64-byte piece of a
+// weight row pairs with 128 bytes of each token row; those are permuted into the lane
+// order of the expanded weight operand (perm16) and used unscaled, so the accumulator
+// holds 16 acc.
+template <int FN, int FM, int U, int RS, bool STORE_ACC, int TK = 1, int NW = 4, bool GRP = false, bool A8 = false>
 __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
     static_assert(!(GRP && STORE_ACC), "group-wise sums are stored dequantized only");
+    static_assert(!(GRP && A8), "group-wise scales with 4-bit activations only");
+    constexpr int XN = A8 ? 2 : 1;       // 16-byte loads per token row per piece
+    constexpr int SH = A8 ? 4 : 8;       // log2 of the operands' combined scale
     __shared__ v4i red[NW][FN * FM][kWave];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int li = lane & 15, g = lane >> 4;
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
         const int64_t tok = fm * 16 + li;
-        xrow[fm] = a.qx + (tok < a.b ? tok : a.b - 1) * kb + g * 16;
+        xrow[fm] = a.qx + (tok < a.b ? tok : a.b - 1) * (A8 ? a.m : kb) + g * 16 * XN;
     }
 
     // Epilogue tiles are dealt to the waves in turn (tile t to wave t % NW). When a
@@ -148,13 +156,20 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
     // one 64-byte piece (128 codes, one group) of every operand row; sw4/sx1: that
     // group's scales (GRP only; s_X pre-multiplied by 2^-8, undoing the x16 x16 of the
     // expanded operands exactly)
-    auto mma = [&](const uint4 (&bw)[FN], const uint4 (&bx)[FM], const float4 (&sw4)[GRP ? FN : 1],
+    auto mma = [&](const uint4 (&bw)[FN], const uint4 (&bx)[FM][XN], const float4 (&sw4)[GRP ? FN : 1],
                    const float (&sx1)[GRP ? FM : 1]) {
         v4i alo[FN], ahi[FN], blo[FM], bhi[FM];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) unpack16(bw[fn], alo[fn], ahi[fn]);
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) unpack16(bx[fm], blo[fm], bhi[fm]);
+        for (int fm = 0; fm < FM; ++fm) {
+            if constexpr (A8) {
+                blo[fm] = perm16(bx[fm][0]);
+                bhi[fm] = perm16(bx[fm][XN - 1]);
+            } else {
+                unpack16(bx[fm][0], blo[fm], bhi[fm]);
+            }
+        }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -179,17 +194,22 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
             for (int fm = 0; fm < FM; ++fm) sx1[fm] = sxp[fm][c * a.b] * 0x1p-8f;
         }
     };
+    auto load_x = [&](int64_t c, uint4 (&bx)[FM][XN]) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int h = 0; h < XN; ++h) bx[fm][h] = *reinterpret_cast<const uint4 *>(xrow[fm] + c * 64 * XN + 16 * h);
+    };
     int64_t c = cb;
     for (; c + U <= ce; c += U) {
-        uint4 bw[U][FN], bx[U][FM];
+        uint4 bw[U][FN], bx[U][FM][XN];
         float4 sw4[U][GRP ? FN : 1];
         float sx1[U][GRP ? FM : 1];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) bw[u][fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (c + u) * 64);
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) bx[u][fm] = *reinterpret_cast<const uint4 *>(xrow[fm] + (c + u) * 64);
+            load_x(c + u, bx[u]);
             load_scales(c + u, sw4[u], sx1[u]);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of its first use
@@ -197,13 +217,12 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
         for (int u = 0; u < U; ++u) mma(bw[u], bx[u], sw4[u], sx1[u]);
     }
     for (; c < ce; ++c) {
-        uint4 bw[FN], bx[FM];
+        uint4 bw[FN], bx[FM][XN];
         float4 sw4[GRP ? FN : 1];
         float sx1[GRP ? FM : 1];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) bw[fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + c * 64);
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) bx[fm] = *reinterpret_cast<const uint4 *>(xrow[fm] + c * 64);
+        load_x(c, bx);
         load_scales(c, sw4, sx1);
         mma(bw, bx, sw4, sx1);
     }
@@ -233,7 +252,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
         const int64_t tok = fm_e * 16 + li;
         const bool store = ch < a.n && tok < a.b;
         if constexpr (STORE_ACC) {
-            if (store) *reinterpret_cast<v4i *>(a.acc + tok * a.n + ch) = sum >> 8;
+            if (store) *reinterpret_cast<v4i *>(a.acc + tok * a.n + ch) = sum >> SH;
         } else {
             v4f y;
             if constexpr (GRP) {
@@ -243,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
                 const float4 sw4 = *reinterpret_cast<const float4 *>(a.sw + (ch < a.n ? ch : a.n - 4));
                 const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
 #pragma unroll
-                for (int v = 0; v < 4; ++v) y[v] = (sxv * swv[v]) * (float)(sum[v] >> 8);
+                for (int v = 0; v < 4; ++v) y[v] = (sxv * swv[v]) * (float)(sum[v] >> SH);
             }
             if (a.lr4) {
                 if (a.r > 0) {
@@ -299,6 +318,15 @@ static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)((a.n + FN * 16 - 1) / (FN * 16)));
     constexpr int TK = RS > 0 && FN * FM <= 4 ? kMaxTSlices / RS : 1;  // partial sums of T the epilogue adds
     constexpr int UG = U > 4 ? U / 2 : U;
+    if (a.a8) {  // W4A8: twice the token bytes per piece, so half the pieces in flight
+        if (a.acc)
+            hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, 0, true, 1, 4, false, true>), grid, dim3(256), 0, stream, a);
+        else if (TK > 1 && a.tks > 1)
+            hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, TK, 4, false, true>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, 1, 4, false, true>), grid, dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
     if (a.acc)
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true>), grid, dim3(256), 0, stream, a);
     else if (a.group && TK > 1 && a.tks > 1)  // group-wise: half the pieces in flight, which leaves room for their scales
@@ -414,7 +442,8 @@ __device__ __forceinline__ void pf_finish(const DualArgs &a, v4f (&y)[FN][FM], i
         }
 }
 
-template <int BN, int BM, int WN, int WM, bool STORE_ACC, bool LR4, int FN, int FM>
+// SH: log2 of the operands' combined scale in acc (8 for 4-bit x 4-bit, 4 for W4A8)
+template <int BN, int BM, int WN, int WM, bool STORE_ACC, bool LR4, int SH, int FN, int FM>
 __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM], int64_t ch0, int64_t tok0, int wn, int wm,
                                             int li, int g) {
     // lane (li, g), register v of tile (fn, fm) holds channel ch_base + 4g + v, token tok_base + li
@@ -425,7 +454,7 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
             for (int fm = 0; fm < FM; ++fm) {
                 const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + 4 * g;
                 const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
-                if (ch < a.n && tok < a.b) *reinterpret_cast<v4i *>(a.acc + tok * a.n + ch) = acc[fn][fm] >> 8;
+                if (ch < a.n && tok < a.b) *reinterpret_cast<v4i *>(a.acc + tok * a.n + ch) = acc[fn][fm] >> SH;
             }
     } else {
         float sxv[FM];
@@ -443,7 +472,7 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) y[fn][fm][v] = (sxv[fm] * swv[v]) * (float)(acc[fn][fm][v] >> 8);
+                for (int v = 0; v < 4; ++v) y[fn][fm][v] = (sxv[fm] * swv[v]) * (float)(acc[fn][fm][v] >> SH);
         }
         pf_finish<BN, BM, WN, WM, LR4>(a, y, ch0, tok0, wn, wm, li, g);
     }
@@ -459,12 +488,22 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 // (one 4-byte direct-to-LDS load per thread, from the group-major scale arrays), and
 // each stage's integer sums are formed from zero and added to the fp32 accumulators
 // times s_X s_W.
-template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false>
-__global__ __launch_bounds__(WN * WM * 64, GRP ? 2 : 3)
+//
+// W4A8 (A8): a token row holds one int8 code per element, 128 bytes per stage, stored as
+// two 64-byte half rows (the first BM rows of the token part hold bytes 0-63 of each
+// token's slice, the next BM rows bytes 64-127), so the layout and the loads above apply
+// unchanged. Lane (li, g) needs codes 32g..32g+31 of its token: chunks 2 (g % 2) and
+// 2 (g % 2) + 1 of half row g / 2, permuted into the expanded weight operand's lane order
+// (perm16); the accumulator holds 16 acc.
+template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false,
+          bool A8 = false>
+__global__ __launch_bounds__(WN * WM * 64, GRP || A8 ? 2 : 3)
 void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     constexpr int NT = WN * WM * 64;
     constexpr int FN = BN / (16 * WN), FM = BM / (16 * WM);
-    constexpr int ROWS = BN + BM;
+    constexpr int XH = A8 ? 2 : 1;              // LDS rows per token row per stage
+    constexpr int ROWS = BN + XH * BM;
+    static_assert(!A8 || (RB == 64 && !GRP && !LR4), "W4A8: 64-byte weight rows, per-token scales");
     static_assert(RB == 64 || RB == 128, "bytes per row per stage");
     constexpr int CPR = RB / 16;                // 16-byte chunks per row per stage
     constexpr int BLK = 16 * RB;                // one block of 16 rows
@@ -497,7 +536,8 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     // in the weight rows or wholly in the token rows, so its address is a uniform tile
     // base (advanced by RB bytes per stage) plus a 32-bit per-lane offset.
     static_assert(NT % 64 == 0 && (BN * CPR) % NT == 0, "each DMA group in one operand");
-    const uint8_t *wbase = a.qw + ch0 * kb, *xbase = a.qx + tok0 * kb;
+    const int64_t xb = A8 ? a.m : kb;           // bytes per token row
+    const uint8_t *wbase = a.qw + ch0 * kb, *xbase = a.qx + tok0 * xb;
     uint32_t off[DPT];
 #pragma unroll
     for (int j = 0; j < DPT; ++j) {
@@ -510,10 +550,11 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
             const int64_t ch = ch0 + row;
             rel = (ch < a.n ? ch : a.n - 1) - ch0;
         } else {
-            const int64_t tok = tok0 + row - BN;
+            const int64_t tok = tok0 + (row - BN) % BM;
             rel = (tok < a.b ? tok : a.b - 1) - tok0;
         }
-        off[j] = (uint32_t)(rel * kb + chunk * 16);
+        // A8: token rows BN + h BM + t hold bytes 64 h .. 64 h + 63 of token t's slice
+        off[j] = (uint32_t)(row < BN ? rel * kb + chunk * 16 : rel * xb + ((row - BN) / BM) * 64 + chunk * 16);
     }
     __shared__ __attribute__((aligned(16))) uint8_t ring[S * SLOT];
     // GRP: this thread's scale: waves 0-1 load s_W of channel ch0 + tid, waves 2-3 s_X of
@@ -536,7 +577,7 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
         for (int j = 0; j < DPT; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds((j * NT) / CPR < BN ? rw : rx,
                                                      (__attribute__((address_space(3))) void *)(dst + (j * NT + wave * kWave) * 16),
-                                                     16, (int)off[j], st * RB, 0, 0);
+                                                     16, (int)off[j], st * RB * ((j * NT) / CPR < BN ? 1 : XH), 0, 0);
         if constexpr (GRP) {
             // group st's row of the group-major scales, from the tile's first channel or token
             const float *sb = wave_u < BN / kWave ? a.sw + (int64_t)st * a.n + ch0 : a.sx + (int64_t)st * a.b + tok0;
@@ -574,6 +615,15 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
         rda[h] = lds_offset(ring) + lane_off + (wn * (BN / WN) / 16) * BLK;
         rdb[h] = lds_offset(ring) + lane_off + ((BN + wm * (BM / WM)) / 16) * BLK;
     }
+    // A8: this lane's two chunks of its half row (64-byte rows: line li / 2, position
+    // (4 (li % 2) + c) ^ (li / 2))
+    uint32_t rdx[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int c = 2 * (g % 2) + e;
+        rdx[e] = lds_offset(ring) + (li / 2) * 128 + ((4 * (li % 2) + c) ^ (li / 2)) * 16 +
+                 ((BN + (g / 2) * BM + wm * (BM / WM)) / 16) * BLK;
+    }
 
     // Step st issues stage st into slot st % S and consumes stage st - (S - 1). Every
     // step issues (past the last stage it loads the last stage again, into a slot no
@@ -596,13 +646,25 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
             if constexpr (GRP) lds_read_scales<OFF>(rsw, rsx, swr, sxr);
 #pragma unroll
             for (int h = 0; h < KS; ++h) {
-                v4i raw[8];
-                lds_read_4x4<OFF, BLK>(rda[h], rdb[h], raw);
                 v4i alo[FN], ahi[FN], blo[FM], bhi[FM];
+                if constexpr (A8) {
+                    v4i raw[12];
+                    lds_read_4x4x4<OFF, BLK>(rda[h], rdx[0], rdx[1], raw);
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn) unpack16(raw[fn], alo[fn], ahi[fn]);
+                    for (int fn = 0; fn < FN; ++fn) unpack16(raw[fn], alo[fn], ahi[fn]);
 #pragma unroll
-                for (int fm = 0; fm < FM; ++fm) unpack16(raw[FN + fm], blo[fm], bhi[fm]);
+                    for (int fm = 0; fm < FM; ++fm) {
+                        blo[fm] = perm16(raw[FN + fm]);
+                        bhi[fm] = perm16(raw[FN + FM + fm]);
+                    }
+                } else {
+                    v4i raw[8];
+                    lds_read_4x4<OFF, BLK>(rda[h], rdb[h], raw);
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) unpack16(raw[fn], alo[fn], ahi[fn]);
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) unpack16(raw[FN + fm], blo[fm], bhi[fm]);
+                }
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -626,14 +688,20 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     if constexpr (GRP)
         pf_finish<BN, BM, WN, WM, false>(a, yg, ch0, tok0, wn, wm, li, g);
     else
-        pf_epilogue<BN, BM, WN, WM, STORE_ACC, LR4>(a, acc, ch0, tok0, wn, wm, li, g);
+        pf_epilogue<BN, BM, WN, WM, STORE_ACC, LR4, A8 ? 4 : 8>(a, acc, ch0, tok0, wn, wm, li, g);
 }
 
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB>
 static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
     const int64_t tiles_n = (a.n + BN - 1) / BN, tiles_m = (a.b + BM - 1) / BM;
     const dim3 grid((unsigned)(tiles_n * tiles_m)), block(WN * WM * 64);
-    if (a.acc)
+    if (a.a8 && a.acc)
+        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, true, false, false, true>), grid, block, 0, stream, a,
+                           (int)tiles_n, (int)tiles_m);
+    else if (a.a8)
+        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, false, false, false, true>), grid, block, 0, stream, a,
+                           (int)tiles_n, (int)tiles_m);
+    else if (a.acc)
         hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, true>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
     else if (a.group)
         hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, false, false, true>), grid, block, 0, stream, a, (int)tiles_n,

@@ -43,12 +43,13 @@ struct LinearLayout {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // group: 0 (one scale per token) or twq::kGroup (s_X group-major [m / kGroup][b])
-LinearLayout linear_layout(int64_t b, int64_t m, int64_t n, int64_t r, int group) {
+// a8: 8-bit activation codes, one byte per element
+LinearLayout linear_layout(int64_t b, int64_t m, int64_t n, int64_t r, int group, int a8 = 0) {
     LinearLayout L{};
     L.plan = twq::plan_act(b, m, r);
     L.direct = r > 0 && L.plan.mode == 1 && L.plan.ks > 1 && L.plan.ks <= twq::dual_max_t_slices(b, n, (int)r);
     L.qx = 0;
-    L.sx = align256((size_t)(b * m / 2));
+    L.sx = align256((size_t)(a8 ? b * m : b * m / 2));
     L.t = L.sx + align256((size_t)b * 4 * (size_t)(group ? m / group : 1));
     L.partials = L.t + (L.direct ? 0 : align256((size_t)(b * r) * 4));
     L.total = L.partials + align256(L.plan.workspace_bytes);
@@ -61,7 +62,7 @@ bool valid_group(int64_t g) { return g == twq::kGroup; }
 // or twq::kGroup and has been validated.
 twq_status quantize_act_impl(const void *x, int64_t b, int64_t m, int group, void *qx, float *sx, const void *l1t,
                              int64_t r, float *t, void *workspace, size_t workspace_bytes, void *stream,
-                             const char *name) {
+                             const char *name, int a8 = 0) {
     if (!valid_b(b) || !valid_m(m) || !valid_r(r)) return TWQ_ERR_SHAPE;
     if (b == 0) return TWQ_OK;
     if (!x || !qx || !sx) return TWQ_ERR_NULL;
@@ -83,6 +84,7 @@ twq_status quantize_act_impl(const void *x, int64_t b, int64_t m, int group, voi
     a.r = (int)r;
     a.t = t;
     a.group = group;
+    a.a8 = a8;
     if (r > 0 && plan.workspace_bytes > 0) a.partials = static_cast<float *>(workspace);
     const hipError_t e = twq::launch_act(a, plan, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TWQ_OK : hip_fail(e, name);
@@ -90,7 +92,7 @@ twq_status quantize_act_impl(const void *x, int64_t b, int64_t m, int group, voi
 
 twq_status dual_linear_impl(const void *qx, const float *sx, const void *qw, const float *sw, const float *t,
                             const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n, int group,
-                            void *stream, const char *name) {
+                            void *stream, const char *name, int a8 = 0) {
     if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return TWQ_ERR_SHAPE;
     if (b == 0 || n == 0) return TWQ_OK;
     if (!qx || !sx || !qw || !sw || !y) return TWQ_ERR_NULL;
@@ -113,20 +115,21 @@ twq_status dual_linear_impl(const void *qx, const float *sx, const void *qw, con
     a.m = m;
     a.n = n;
     a.group = group;
+    a.a8 = a8;
     const hipError_t e = twq::launch_dual_linear(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TWQ_OK : hip_fail(e, name);
 }
 
 twq_status linear_impl(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t, int64_t r,
                        void *y, int64_t b, int64_t m, int64_t n, int group, void *workspace, size_t workspace_bytes,
-                       void *stream, const char *name) {
+                       void *stream, const char *name, int a8 = 0) {
     if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return TWQ_ERR_SHAPE;
     if (b == 0 || n == 0) return TWQ_OK;
     if (!x || !qw || !sw || !y) return TWQ_ERR_NULL;
     if (r > 0 && (!l1t || !l2t)) return TWQ_ERR_NULL;
     if (!aligned16(x) || !aligned16(qw) || !aligned16(sw) || !aligned16(y)) return TWQ_ERR_ALIGN;
     if (r > 0 && (!aligned16(l1t) || !aligned16(l2t))) return TWQ_ERR_ALIGN;
-    const LinearLayout L = linear_layout(b, m, n, r, group);
+    const LinearLayout L = linear_layout(b, m, n, r, group, a8);
     if (!workspace || workspace_bytes < L.total) return TWQ_ERR_WORKSPACE;
     if (!aligned16(workspace)) return TWQ_ERR_ALIGN;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -144,6 +147,7 @@ twq_status linear_impl(const void *x, const void *qw, const float *sw, const voi
     act.partials = reinterpret_cast<float *>(ws + L.partials);
     act.keep_partials = L.direct;
     act.group = group;
+    act.a8 = a8;
     hipError_t e = twq::launch_act(act, L.plan, st);
     if (e != hipSuccess) return hip_fail(e, name);
 
@@ -163,6 +167,7 @@ twq_status linear_impl(const void *x, const void *qw, const float *sw, const voi
     a.m = m;
     a.n = n;
     a.group = group;
+    a.a8 = a8;
     e = twq::launch_dual_linear(a, st);
     return e == hipSuccess ? TWQ_OK : hip_fail(e, name);
 }
@@ -335,6 +340,46 @@ twq_status twq_linear_grouped(const void *x, const void *qw, const float *sw, co
     if (!valid_group(g)) return TWQ_ERR_UNSUPPORTED;
     return linear_impl(x, qw, sw, l1t, l2t, r, y, b, m, n, (int)g, workspace, workspace_bytes, stream,
                        "twq_linear_grouped");
+}
+
+twq_status twq_quantize_act_a8(const void *x, int64_t b, int64_t m, void *qx, float *sx, const void *l1t, int64_t r,
+                               float *t, void *workspace, size_t workspace_bytes, void *stream) {
+    return quantize_act_impl(x, b, m, 0, qx, sx, l1t, r, t, workspace, workspace_bytes, stream, "twq_quantize_act_a8", 1);
+}
+
+twq_status twq_dual_linear_a8(const void *qx, const float *sx, const void *qw, const float *sw, const float *t,
+                              const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n, void *stream) {
+    return dual_linear_impl(qx, sx, qw, sw, t, l2t, r, y, b, m, n, 0, stream, "twq_dual_linear_a8", 1);
+}
+
+size_t twq_linear_a8_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r) {
+    if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return 0;
+    return linear_layout(b, m, n, r, 0, 1).total;
+}
+
+twq_status twq_linear_a8(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t, int64_t r,
+                         void *y, int64_t b, int64_t m, int64_t n, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    return linear_impl(x, qw, sw, l1t, l2t, r, y, b, m, n, 0, workspace, workspace_bytes, stream, "twq_linear_a8", 1);
+}
+
+twq_status twq_debug_residual_acc_a8(const void *qx, const void *qw, int32_t *acc, int64_t b, int64_t m, int64_t n,
+                                     void *stream) {
+    if (!valid_b(b) || !valid_m(m) || !valid_n(n)) return TWQ_ERR_SHAPE;
+    if (b == 0 || n == 0) return TWQ_OK;
+    if (!qx || !qw || !acc) return TWQ_ERR_NULL;
+    if (!aligned16(qx) || !aligned16(qw) || !aligned16(acc)) return TWQ_ERR_ALIGN;
+    twq::DualArgs a{};
+    a.qx = static_cast<const uint8_t *>(qx);
+    a.qw = static_cast<const uint8_t *>(qw);
+    a.acc = acc;
+    a.tks = 1;
+    a.b = b;
+    a.m = m;
+    a.n = n;
+    a.a8 = 1;
+    const hipError_t e = twq::launch_dual_linear(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_debug_residual_acc_a8");
 }
 
 }  // extern "C"

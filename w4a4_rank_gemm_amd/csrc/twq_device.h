@@ -41,6 +41,20 @@ __device__ __forceinline__ int quant_code_fast(float v, float s, float inv) {
     return (int)r;
 }
 
+// The 8-bit activation code of eq. (1) (q_max = 127) from inv = fl32(1 / s), exact
+// in the same way as quant_code_fast: for |v / s| <= 127, t = fl32(v inv) lies within
+// 1.6e-5 of v / s and fl32(v / s) within 7.6e-6, so only a t within 2^-15 of a
+// half-integer takes the correctly rounded division.
+constexpr float kQMax8 = 127.0f;  // 2^(k-1) - 1 for k = 8
+__device__ __forceinline__ int quant_code8_fast(float v, float s, float inv) {
+#pragma clang fp contract(off)
+    float t = v * inv;
+    float r = __builtin_rintf(t);
+    if (__builtin_fabsf(t - r) >= 0.5f - 0x1p-15f) r = __builtin_rintf(v / s);
+    r = __builtin_fminf(__builtin_fmaxf(r, -kQMax8), kQMax8);
+    return (int)r;
+}
+
 // Eight codes (elements e0..e7 of a row, in order) into one dword of the packed
 // format: element 2t in the low nibble of byte t, element 2t+1 in its high nibble.
 __device__ __forceinline__ uint32_t pack8(const int q[8]) {
@@ -91,6 +105,22 @@ __device__ __forceinline__ void unpack16(const uint4 raw, v4i &lo, v4i &hi) {
 
 __device__ __forceinline__ void unpack16(const v4i raw, v4i &lo, v4i &hi) {
     unpack16(make_uint4((uint32_t)raw[0], (uint32_t)raw[1], (uint32_t)raw[2], (uint32_t)raw[3]), lo, hi);
+}
+
+// 16 int8 codes (elements 0..15 of a K run, in order) -> one int8 MFMA operand in the
+// lane-local K order unpack16 gives the packed 4-bit codes (1, 3, 5, 7, 0, 2, 4, 6,
+// 9, ..., 8, ...), so an 8-bit operand pairs element for element with a 4-bit one.
+__device__ __forceinline__ v4i perm16(const uint4 raw) {
+    v4i r;
+    r[0] = (int)__builtin_amdgcn_perm(raw.y, raw.x, 0x07050301u);
+    r[1] = (int)__builtin_amdgcn_perm(raw.y, raw.x, 0x06040200u);
+    r[2] = (int)__builtin_amdgcn_perm(raw.w, raw.z, 0x07050301u);
+    r[3] = (int)__builtin_amdgcn_perm(raw.w, raw.z, 0x06040200u);
+    return r;
+}
+
+__device__ __forceinline__ v4i perm16(const v4i raw) {
+    return perm16(make_uint4((uint32_t)raw[0], (uint32_t)raw[1], (uint32_t)raw[2], (uint32_t)raw[3]));
 }
 
 __device__ __forceinline__ v4i mfma_i8(const v4i a, const v4i b, v4i c) {
@@ -149,6 +179,32 @@ __device__ __forceinline__ void lds_read_4x4(uint32_t a, uint32_t b, v4i (&r)[8]
         "s_waitcnt lgkmcnt(0)"
         : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7])
         : "v"(a), "v"(b), "n"(OFF), "n"(OFF + BLK), "n"(OFF + 2 * BLK), "n"(OFF + 3 * BLK)
+        : "memory");
+}
+
+// Twelve operand reads of one stage: four consecutive 1 KB blocks from each of the
+// addresses a, b0 and b1 (each plus OFF), completed before returning, for the same
+// reason and in the same way as lds_read_4x4.
+template <int OFF, int BLK>
+__device__ __forceinline__ void lds_read_4x4x4(uint32_t a, uint32_t b0, uint32_t b1, v4i (&r)[12]) {
+    static_assert(OFF >= 0 && OFF + 3 * BLK < 65536, "ds_read immediate offset");
+    asm volatile(
+        "ds_read_b128 %0, %12 offset:%15\n\t"
+        "ds_read_b128 %1, %12 offset:%16\n\t"
+        "ds_read_b128 %2, %12 offset:%17\n\t"
+        "ds_read_b128 %3, %12 offset:%18\n\t"
+        "ds_read_b128 %4, %13 offset:%15\n\t"
+        "ds_read_b128 %5, %13 offset:%16\n\t"
+        "ds_read_b128 %6, %13 offset:%17\n\t"
+        "ds_read_b128 %7, %13 offset:%18\n\t"
+        "ds_read_b128 %8, %14 offset:%15\n\t"
+        "ds_read_b128 %9, %14 offset:%16\n\t"
+        "ds_read_b128 %10, %14 offset:%17\n\t"
+        "ds_read_b128 %11, %14 offset:%18\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
+          "=v"(r[8]), "=v"(r[9]), "=v"(r[10]), "=v"(r[11])
+        : "v"(a), "v"(b0), "v"(b1), "n"(OFF), "n"(OFF + BLK), "n"(OFF + 2 * BLK), "n"(OFF + 3 * BLK)
         : "memory");
 }
 

@@ -38,6 +38,7 @@ struct ActArgs {
     int keep_partials;  // ks > 1: leave T as partial sums (the caller's dual launch adds them)
     int group;          // 0: one scale per token row, s_X [b]; kGroup: one scale per kGroup
                         // consecutive elements of a row, s_X group-major [m / kGroup][b]
+    int a8;             // 8-bit activations (q_max = 127): qx holds one int8 code per element [b][m]
 };
 
 // Group size of the group-wise variant: one K stage of every main loop.
@@ -73,6 +74,7 @@ struct DualArgs {
     const float *sh;   // [b]
     const uint8_t *ql2;// [n][r/2] packed Q_L2
     int group;         // kGroup: group-wise scales, sx [m / kGroup][b] and sw [m / kGroup][n]
+    int a8;            // 8-bit activation codes: qx int8 [b][m] (W4A8)
 };
 
 hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream);
