@@ -59,6 +59,12 @@ def dual_linear_grouped_bytes(b, m, n, r, g):
     return b * m // 2 + 4 * b * (m // g) + m * n // 2 + 4 * n * (m // g) + 4 * b * r + 2 * n * r + 2 * b * n
 
 
+def dual_linear_a8_bytes(b, m, n, r):
+    """Algorithmic bytes of one twq_dual_linear_a8 launch: as dual_linear_bytes with one
+    byte per activation code."""
+    return b * m + 4 * b + m * n // 2 + 4 * n + 4 * b * r + 2 * n * r + 2 * b * n
+
+
 def call_bytes_lr4(b, m, n, r):
     """Compulsory HBM bytes of one call with the int4 low-rank branch: X fp16, Q_W, s_W,
     Q_L1 and Q_L2 (4-bit), c, Y fp16."""
@@ -135,6 +141,34 @@ def _cpu_baseline_grouped(d, g, budget_s=12.0):
             "sample": f"{calls} calls on the first {rows} of {b} tokens (b={b}, m={m}, n={n}, r={r}, "
                       f"groups of {g}) in {el:.1f} s, scaled to the whole batch; weights quantized once "
                       "outside the timing"}
+
+
+def _cpu_baseline_a8(d, budget_s=12.0):
+    """The W4A8 oracle on the host: per-call work with weights pre-quantized."""
+    import numpy as np
+
+    import oracle
+    x, w, l1t, l2t = d["x"], d["w_res"], d["l1t"], d["l2t"]
+    b, m = x.shape
+    n, r = w.shape[0], l1t.shape[0]
+    qw, _, sw = oracle.quantize_weight(w)  # offline packing, not timed
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        qx, sx = oracle.quantize_act_a8(x)
+        acc = oracle.residual_acc(qx, qw)
+        y = sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] * acc
+        if r:
+            y += oracle.lowrank_out(oracle.lowrank_t(x, l1t), l2t)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 1000:
+            break
+    sec = el / calls
+    return {"value": layer_ops(b, m, n, r) / sec / 1e12, "unit": "TOPS", "cores": oracle.max_threads(),
+            "kind": "oracle", "ms_per_call": sec * 1e3,
+            "sample": f"{calls} whole W4A8 calls of the same workload (b={b}, m={m}, n={n}, r={r}) "
+                      f"in {el:.1f} s; weights quantized once outside the timing"}
 
 
 def _cpu_baseline(d, budget_s=12.0, lr4=False):
@@ -296,6 +330,8 @@ def main():
                          "+ twq_dual_linear_lr4 with 4-bit L1, L2 and H")
     ap.add_argument("--group", type=int, choices=(0, 128), default=0,
                     help="128: group-wise scales (twq_*_grouped entry points, groups of 128 along K)")
+    ap.add_argument("--act-bits", type=int, choices=(4, 8), default=4,
+                    help="8: W4A8 (twq_*_a8 entry points, 8-bit per-token activation codes)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate over (0: auto)")
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
@@ -331,8 +367,11 @@ def main():
     grp = args.group
     if lr4 and args.path != "linear":
         ap.error("--lowrank int4 has one call sequence; leave --path at its default")
+    a8 = args.act_bits == 8
     if lr4 and grp:
         ap.error("--group applies to the fp16 low-rank branch only")
+    if a8 and (lr4 or grp):
+        ap.error("--act-bits 8 takes per-token scales and the fp16 low-rank branch")
     per_copy = (call_bytes_lr4(b, m, n, r) if lr4 else call_bytes_grouped(b, m, n, r, grp) if grp
                 else call_bytes(b, m, n, r))
     copies = args.copies or max(1, math.ceil(ROTATE_BYTES / per_copy))
@@ -348,7 +387,7 @@ def main():
         s_ = {
             "x": x0.clone(), "qw": qw0.clone(), "sw": sw0.clone(),
             "l1t": l10.clone() if (r and not lr4) else None, "l2t": l20.clone() if (r and not lr4) else None,
-            "qx": torch.empty((b, m // 2), dtype=torch.uint8, device=dev),
+            "qx": torch.empty((b, m) if a8 else (b, m // 2), dtype=torch.uint8, device=dev),
             "sx": torch.empty((m // grp, b) if grp else (b,), dtype=torch.float32, device=dev),
             "t": torch.empty((b, r), dtype=torch.float32, device=dev) if (r and not lr4) else None,
             "y": torch.empty((b, n), dtype=torch.float16, device=dev),
@@ -364,10 +403,15 @@ def main():
     L = twq.lib()
     ws, wsb = twq._workspace(dev, max(L.twq_quantize_act_workspace_bytes(b, m, r),
                                       L.twq_linear_grouped_workspace_bytes(b, m, n, r, grp) if grp
+                                      else L.twq_linear_a8_workspace_bytes(b, m, n, r) if a8
                                       else L.twq_linear_workspace_bytes(b, m, n, r)))
     P = lambda t: None if t is None else twq.ctypes.c_void_p(t.data_ptr())
 
     def layer(s, stream):
+        if a8:
+            twq._check(L.twq_linear_a8(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["l1t"]), P(s["l2t"]), r, P(s["y"]),
+                                       b, m, n, P(ws), wsb, stream), "twq_linear_a8")
+            return
         if grp:
             twq._check(L.twq_linear_grouped(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["l1t"]), P(s["l2t"]), r,
                                             P(s["y"]), b, m, n, grp, P(ws), wsb, stream), "twq_linear_grouped")
@@ -376,6 +420,10 @@ def main():
                                 b, m, n, P(ws), wsb, stream), "twq_linear")
 
     def quant(s, stream):
+        if a8:
+            twq._check(L.twq_quantize_act_a8(P(s["x"]), b, m, P(s["qx"]), P(s["sx"]), P(s["l1t"]), r, P(s["t"]),
+                                             P(ws), wsb, stream), "twq_quantize_act_a8")
+            return
         if grp:
             twq._check(L.twq_quantize_act_grouped(P(s["x"]), b, m, grp, P(s["qx"]), P(s["sx"]), P(s["l1t"]), r,
                                                   P(s["t"]), P(ws), wsb, stream), "twq_quantize_act_grouped")
@@ -387,6 +435,10 @@ def main():
                                              P(s["qh"]), P(s["sh"]), b, m, stream), "twq_lowrank_requant")
 
     def dual(s, stream):
+        if a8:
+            twq._check(L.twq_dual_linear_a8(P(s["qx"]), P(s["sx"]), P(s["qw"]), P(s["sw"]), P(s["t"]), P(s["l2t"]),
+                                            r, P(s["y"]), b, m, n, stream), "twq_dual_linear_a8")
+            return
         if lr4:
             twq._check(L.twq_dual_linear_lr4(P(s["qx"]), P(s["sx"]), P(s["qw"]), P(s["sw"]), P(s["qh"]),
                                              P(s["sh"]), P(s["ql2"]), r, P(s["y"]), b, m, n, stream),
@@ -476,9 +528,9 @@ def main():
     tops = ops / (ms_step * 1e-3) / 1e12
     decode = b <= 64
     kbytes = (dual_linear_lr4_bytes(b, m, n, r) if lr4 else dual_linear_grouped_bytes(b, m, n, r, grp) if grp
-              else dual_linear_bytes(b, m, n, r))
+              else dual_linear_a8_bytes(b, m, n, r) if a8 else dual_linear_bytes(b, m, n, r))
     cbytes = per_copy
-    traffic = None if (lr4 or grp) else measured_traffic(args.config)
+    traffic = None if (lr4 or grp or a8) else measured_traffic(args.config)
     if decode:
         ach = kbytes / (us_dual * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -487,12 +539,13 @@ def main():
         ach = 2 * b * m * n / (us_dual * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": traffic}
-    roof["kernel"] = "twq_dual_linear_lr4" if lr4 else "twq_dual_linear_grouped" if grp else "twq_dual_linear"
+    roof["kernel"] = ("twq_dual_linear_lr4" if lr4 else "twq_dual_linear_grouped" if grp else
+                      "twq_dual_linear_a8" if a8 else "twq_dual_linear")
     roof["kernel_us"] = round(us_dual, 3)
     roof["algorithmic_bytes"] = kbytes
     roof["algorithmic_int8_ops"] = 2 * b * m * n
 
-    sfx = "_grouped" if grp else ""
+    sfx = "_grouped" if grp else "_a8" if a8 else ""
     if lr4:
         entry_points = "twq_quantize_act+twq_lowrank_requant+twq_dual_linear_lr4"
     elif args.path == "linear":
@@ -512,11 +565,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("int4 codes on i8 MFMA (int32 acc), int4 low-rank on i8 MFMA" if lr4 else
+                  "int4 weight x int8 activation codes on i8 MFMA (int32 acc) + fp16 low-rank (fp32 acc)" if a8 else
                   "int4 codes on i8 MFMA (int32 acc) + fp16 low-rank (fp32 acc)"),
         "data": "synthetic",
         "config": {"workload": f"{args.config}: b={b} m={m} n={n} r={r}", "b": b, "m": m, "n": n, "r": r,
                    "weight_copies_rotated": copies, "launch": "eager" if args.eager else "hip_graph",
-                   "lowrank": args.lowrank, "group": grp or "per token / per channel",
+                   "lowrank": args.lowrank, "group": grp or "per token / per channel", "act_bits": args.act_bits,
                    "entry_points": entry_points,
                    "call_bytes": cbytes,
                    "hbm_frac_whole_call": round(cbytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -525,7 +579,8 @@ def main():
     }
     if not args.no_cpu:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = _cpu_baseline_grouped(d, grp) if grp else _cpu_baseline(d, lr4=lr4)
+        out["cpu_baseline"] = (_cpu_baseline_grouped(d, grp) if grp else _cpu_baseline_a8(d) if a8
+                               else _cpu_baseline(d, lr4=lr4))
         out["cpu_baseline"]["host"] = platform.processor() or platform.machine()
     print(json.dumps(out), flush=True)
 
