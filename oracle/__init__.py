@@ -422,3 +422,32 @@ def unpack_codes(packed):
     out[..., 0::2] = lo
     out[..., 1::2] = hi
     return out
+
+
+# ---- offline preparation: SVD split and folding of given transforms -------------------
+#
+# TwinQuant page 1, section 4.1 (eq. (6) and the factors defined below it): with an
+# orthogonal Q (m x m) acting on the activations and an invertible G (r x r) acting on
+# the rank space, the layer's factors become U' = Q^-1 U G, V' = G^-1 V and R' = Q^-1 R,
+# and the layer is fed X Q, so that (X Q)(U' V' + R') = X (U V + R) = X W. Learning Q and
+# G needs calibration data and is not done here; they are inputs.
+
+def fold_split(w_nm, r, q=None, g=None):
+    """Plain fp64 definition. w_nm: W^T (fp32 [n][m], nn.Linear layout), r: rank,
+    q: orthogonal [m][m] or None (identity), g: invertible [r][r] or None (identity).
+    U S V^T = W (LAPACK SVD), U_r = U[:, :r] sqrt(S_r), V_r = sqrt(S_r) V^T[:r];
+    U' = Q^T U_r G and V' = G^-1 V_r rounded to fp16; R' = Q^T W - U' V' from those
+    rounded factors, rounded to fp32. Returns (l1t' fp16 [r][m], l2t' fp16 [n][r],
+    w_res' fp32 [n][m])."""
+    w = np.asarray(w_nm, np.float64).T  # m x n
+    m, n = w.shape
+    qm = np.eye(m) if q is None else np.asarray(q, np.float64)
+    gm = np.eye(r) if g is None else np.asarray(g, np.float64)
+    u, s, vt = np.linalg.svd(w, full_matrices=False)
+    rs = np.sqrt(s[:r])
+    u_r = u[:, :r] * rs[None, :]
+    v_r = rs[:, None] * vt[:r]
+    u_f = (qm.T @ u_r @ gm).astype(np.float16)
+    v_f = np.linalg.solve(gm, v_r).astype(np.float16)
+    r_f = (qm.T @ w - u_f.astype(np.float64) @ v_f.astype(np.float64)).astype(np.float32)
+    return np.ascontiguousarray(u_f.T), np.ascontiguousarray(v_f.T), np.ascontiguousarray(r_f.T)

@@ -1,0 +1,82 @@
+"""Offline split and folding on the GPU (TwinQuant page 1, section 4.1: U' = Q^-1 U G,
+V' = G^-1 V, R' = Q^-1 R, the layer fed X Q) against the oracle's plain fp64
+definition, and the fused layer on the folded operands against the oracle.
+
+The singular vectors of an SVD are unique only up to sign, so the factors are compared
+through their product U' V' (and the residual), which is unique when the r-th and
+(r+1)-th singular values are apart (the test weights have a decaying spectrum)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w4a4_rank_gemm_amd as twq
+from w4a4_rank_gemm_amd import prep
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(n, m, r, seed, gap=False):
+    rng = synth.rng_for(seed)
+    k = min(n, m)
+    # gap: the top r singular values well above the rest, so that the randomized range
+    # finder (four power iterations) converges to the same subspace as a dense SVD
+    spectrum = (np.concatenate([np.geomspace(4.0, 1.0, r), np.geomspace(0.02, 0.001, k - r)]) if gap
+                else np.geomspace(4.0, 0.05, k))
+    a, _ = np.linalg.qr(rng.standard_normal((n, min(n, m))))
+    b, _ = np.linalg.qr(rng.standard_normal((m, min(n, m))))
+    w = ((a * spectrum[None, :]) @ b.T).astype(np.float32)
+    q, _ = np.linalg.qr(rng.standard_normal((m, m)))
+    # an invertible G of condition number at most 4 (a rotation times scales in [0.5, 2]):
+    # the fp16 T of the layer is exact only to 2^-11 |T|, and T L2 with T = (X Q) U' G
+    # amplifies that by the conditioning of G, which a learned G keeps small
+    rot, _ = np.linalg.qr(rng.standard_normal((r, r)))
+    g = rot * rng.uniform(0.5, 2.0, r)[None, :]
+    x = (rng.standard_normal((24, m)) * 2).astype(np.float16)
+    return w, q, g, x
+
+
+@pytest.mark.parametrize("n,m,r,method", [(384, 512, 32, "exact"), (1024, 2048, 64, "randomized")])
+def test_fold_split_matches_oracle_and_layer(n, m, r, method):
+    w, q, g, x = _case(n, m, r, 900 + r, gap=method == "randomized")
+    dev = torch.device("cuda:0")
+    l1t, l2t, w_res = prep.fold_split(torch.from_numpy(w).to(dev), r, torch.from_numpy(q).to(dev),
+                                      torch.from_numpy(g).to(dev), method=method, seed=1)
+    torch.cuda.synchronize()
+    ol1t, ol2t, ow_res = oracle.fold_split(w, r, q, g)
+    uv = l1t.double().T @ l2t.double().T
+    ou, ov = torch.from_numpy(ol1t.astype(np.float64)).to(dev).T, torch.from_numpy(ol2t.astype(np.float64)).to(dev).T
+    ouv = ou @ ov
+    # Both sides hold the exact U' V' up to the fp16 rounding of their own factors, which
+    # is at most 2^-11 relative per element, so each product lies within 2^-10 |U'| |V'|
+    # (elementwise) of the exact one. The factors themselves may differ between the
+    # sides (singular vectors are defined up to sign, and G mixes the rank space), so the
+    # two rounding bounds add; G also makes |U'| |V'| much larger than |U' V'|.
+    gu, gv = l1t.double().T, l2t.double().T
+    bound = 2.0 ** -10 * (ou.abs() @ ov.abs() + gu.abs() @ gv.abs()) + 1e-9
+    assert ((uv - ouv).abs() <= bound).all()
+    assert ((w_res.double().T - torch.from_numpy(ow_res).to(dev).double().T).abs() <= bound + 1e-6).all()
+    # the fold leaves the real product unchanged: (X Q)(U' V' + R') = X W
+    xd = torch.from_numpy(x.astype(np.float64)).to(dev)
+    xq = xd @ torch.from_numpy(q).to(dev)
+    ref = xd @ torch.from_numpy(w.astype(np.float64)).to(dev).T
+    got = xq @ (uv + w_res.double().T)
+    assert (got - ref).abs().max().item() <= 1e-5 * ref.abs().max().item()
+    # the fused layer on the folded operands, fed X Q, against the oracle on the same operands
+    xq16 = xq.to(torch.float16)
+    qw, sw = twq.pack_weight(w_res)
+    y = twq.linear(xq16, qw, sw, l1t, l2t)
+    torch.cuda.synchronize()
+    ref_layer = oracle.dual_linear(xq16.cpu().numpy(), w_res.cpu().numpy(), l1t.cpu().numpy(), l2t.cpu().numpy())
+    err = np.abs(y.cpu().numpy().astype(np.float64) - ref_layer["y"]).max()
+    assert err <= 2e-3 * np.abs(ref_layer["y"]).max()
+
+
+def test_fold_split_identity_is_plain_split():
+    w, _, _, _ = _case(96, 128, 16, 950)
+    dev = torch.device("cuda:0")
+    l1t, l2t, w_res = prep.fold_split(torch.from_numpy(w).to(dev), 16)
+    torch.cuda.synchronize()
+    back = w_res.double() + l2t.double() @ l1t.double()
+    assert (back - torch.from_numpy(w).to(dev).double()).abs().max().item() <= 1e-6

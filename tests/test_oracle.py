@@ -582,3 +582,50 @@ def test_a8_library_matmul_and_sampled(oracle_lib):
     rows, cols = rng.integers(0, 9, 40), rng.integers(0, 40, 40)
     acc, y = oracle_lib.dual_linear_a8_sampled(d["x"], d["w_res"], d["l1t"], d["l2t"], rows, cols)
     assert (acc == out["acc"][rows, cols]).all() and (y == out["y"][rows, cols]).all()
+
+
+# ---------------------------------------------------------------- offline folding of Q and G
+
+def _qg(m, r, seed):
+    rng = synth.rng_for(seed)
+    q, _ = np.linalg.qr(rng.standard_normal((m, m)))
+    g = np.eye(r) + 0.3 * rng.standard_normal((r, r))
+    return q, g
+
+
+def test_fold_invariance_and_eckart_young(oracle_lib):
+    """(X Q)(U' V' + R') = X W for any orthogonal Q and invertible G (the split is exact
+    against the stored factors); U' V' = Q^T U V does not depend on G; and ||R'||_F is the
+    tail of the spectrum (Eckart-Young) up to the fp16 rounding of the factors."""
+    rng = synth.rng_for(60)
+    n, m, r = 40, 48, 8
+    w = (rng.standard_normal((n, m)) * np.linspace(2.0, 0.1, m)[None, :]).astype(np.float32)
+    x = rng.standard_normal((5, m))
+    q, g = _qg(m, r, 61)
+    l1t, l2t, w_res = oracle_lib.fold_split(w, r, q, g)
+    uv = l1t.T.astype(np.float64) @ l2t.T.astype(np.float64)          # U' V'  (m x n)
+    total = uv + w_res.T.astype(np.float64)                            # U' V' + R'
+    ref = x @ w.T.astype(np.float64)
+    np.testing.assert_allclose((x @ q) @ total, ref, rtol=0, atol=1e-5 * np.abs(ref).max())
+    # G cancels in the product of the factors
+    l1b, l2b, _ = oracle_lib.fold_split(w, r, q, np.eye(r))
+    uv_b = l1b.T.astype(np.float64) @ l2b.T.astype(np.float64)
+    np.testing.assert_allclose(uv, uv_b, rtol=0, atol=5e-3 * np.abs(uv_b).max())
+    s = np.linalg.svd(w.astype(np.float64), compute_uv=False)
+    tail = np.sqrt((s[r:] ** 2).sum())
+    assert abs(np.linalg.norm(w_res.astype(np.float64)) - tail) <= 2e-3 * s[0]
+
+
+def test_fold_identity_and_rank_zero(oracle_lib):
+    """Q = I and G = I give the plain split: the factors span the top-r singular space and
+    the residual is W minus their product; r = 0 leaves W whole."""
+    rng = synth.rng_for(62)
+    w = rng.standard_normal((24, 32)).astype(np.float32)
+    l1t, l2t, w_res = oracle_lib.fold_split(w, 4, None, None)
+    np.testing.assert_allclose(w_res.astype(np.float64) + l2t.astype(np.float64) @ l1t.astype(np.float64),
+                               w.astype(np.float64), rtol=0, atol=1e-6)
+    u, s, vt = np.linalg.svd(w.T.astype(np.float64))
+    proj = u[:, :4] @ u[:, :4].T  # the factors' column space is the top-4 left singular space of W
+    np.testing.assert_allclose(proj @ l1t.T.astype(np.float64), l1t.T.astype(np.float64), atol=2e-3)
+    l1t0, l2t0, w_res0 = oracle_lib.fold_split(w, 0, None, None)
+    assert l1t0.shape == (0, 32) and l2t0.shape == (24, 0) and (w_res0 == w).all()

@@ -1,0 +1,79 @@
+"""Offline preparation of a TwinQuant layer on the GPU: the rank-r SVD split of the
+weight and the folding of given transforms into its factors.
+
+TwinQuant page 1, section 2, eq. (3): W = U V + R with a rank-r low-rank pair from the
+SVD and a residual R. Page 1, section 4.1 (eq. (6) and the factors below it): an
+orthogonal Q (m x m) on the activations and an invertible G (r x r) on the rank space
+give U' = Q^-1 U G, V' = G^-1 V and R' = Q^-1 R, and the layer is fed X Q; the real
+product is unchanged, (X Q)(U' V' + R') = X W. Learning Q and G needs calibration data
+and is not part of this library: they come in as inputs.
+
+This runs once per layer, before serving, on the platform's dense linear algebra (fp64
+matrix products, QR and SVD); its outputs feed twq_pack_weight and the fused layer.
+"""
+from __future__ import annotations
+
+import torch
+
+
+def _top_svd(w: torch.Tensor, r: int, method: str, seed: int):
+    """Top-r singular triplets of w (fp64, on its device): (u [m][r], s [r], vt [r][n])."""
+    if method == "exact":
+        u, s, vt = torch.linalg.svd(w, full_matrices=False)
+        return u[:, :r], s[:r], vt[:r]
+    # randomized range finder with power iterations (Halko, Martinsson and Tropp 2011,
+    # algorithms 4.4 and 5.1): oversampling 16, 4 power iterations
+    k = min(r + 16, min(w.shape))
+    gen = torch.Generator(device=w.device).manual_seed(seed)
+    omega = torch.randn((w.shape[1], k), generator=gen, device=w.device, dtype=w.dtype)
+    y = torch.linalg.qr(w @ omega).Q
+    for _ in range(4):
+        z = torch.linalg.qr(w.T @ y).Q
+        y = torch.linalg.qr(w @ z).Q
+    ub, s, vt = torch.linalg.svd(y.T @ w, full_matrices=False)
+    return (y @ ub)[:, :r], s[:r], vt[:r]
+
+
+def fold_split(w_nm: torch.Tensor, r: int, q: torch.Tensor | None = None, g: torch.Tensor | None = None,
+               method: str = "auto", seed: int = 0):
+    """Split and fold one layer on the GPU.
+
+    w_nm: W^T, fp32 [n][m] (nn.Linear layout); r: rank; q: orthogonal [m][m] or None
+    (identity); g: invertible [r][r] or None (identity). U' = Q^T U_r G and V' =
+    G^-1 V_r are rounded to fp16, and R' = Q^T W - U' V' is formed from those rounded
+    factors in fp64 and rounded to fp32, so the split is exact against the factors the
+    layer is given. method: "exact" (dense SVD), "randomized", or "auto" (exact up to
+    4096 on the longer side). Returns (l1t' fp16 [r][m], l2t' fp16 [n][r], w_res' fp32
+    [n][m]) on w_nm's device; the layer is then called on X Q."""
+    if w_nm.dim() != 2 or w_nm.device.type != "cuda":
+        raise ValueError("w_nm must be a 2-D GPU tensor")
+    n, m = w_nm.shape
+    if not 0 <= r <= min(m, n):
+        raise ValueError(f"rank {r} must lie in [0, min(m, n) = {min(m, n)}]")
+    dev = w_nm.device
+    w = w_nm.to(torch.float64).T.contiguous()  # m x n
+    if q is not None and q.shape != (m, m):
+        raise ValueError("q must be [m][m]")
+    if g is not None and g.shape != (r, r):
+        raise ValueError("g must be [r][r]")
+    qt = None if q is None else q.to(dev, torch.float64).T
+    w_rot = w if qt is None else qt @ w
+    if r == 0:
+        return (torch.empty((0, m), dtype=torch.float16, device=dev), torch.empty((n, 0), dtype=torch.float16, device=dev),
+                w_rot.T.to(torch.float32).contiguous())
+    if method == "auto":
+        method = "exact" if max(m, n) <= 4096 else "randomized"
+    u, s, vt = _top_svd(w, r, method, seed)
+    rs = torch.sqrt(s)
+    u_r = u * rs[None, :]
+    v_r = rs[:, None] * vt
+    if qt is not None:
+        u_r = qt @ u_r
+    if g is not None:
+        gd = g.to(dev, torch.float64)
+        u_r = u_r @ gd
+        v_r = torch.linalg.solve(gd, v_r)
+    u_f = u_r.to(torch.float16)
+    v_f = v_r.to(torch.float16)
+    r_f = (w_rot - u_f.to(torch.float64) @ v_f.to(torch.float64)).to(torch.float32)
+    return u_f.T.contiguous(), v_f.T.contiguous(), r_f.T.contiguous()
