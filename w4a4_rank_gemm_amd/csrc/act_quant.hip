@@ -371,14 +371,15 @@ ActPlan plan_act(int64_t b, int64_t m, int64_t r) {
         pl.ks = (int)ks;
     } else {
         // few tokens: every token x one 16-rank tile x one K slice per CTA, slices of
-        // about 16 KB of X and L1 each (a compute unit streams only tens of GB/s, so
-        // the read is spread wide); each short token row is quantized by nsl CTAs
+        // about 32 KB of X and L1 each (a compute unit streams only tens of GB/s, so
+        // the read is spread wide; smaller slices measured slower, their partial sums
+        // costing more than they spread); each short token row is quantized by nsl CTAs
         pl.mode = 1;
         pl.fm = (int)((b + 15) / 16);
         pl.row_tile = pl.fm * 16;
         pl.row_tiles = (int)(r / 16);
         const int64_t bytes = m * (16 * pl.fm + 16) * 2;
-        int64_t ks = pow2_floor(bytes / 16384 > 0 ? bytes / 16384 : 1);
+        int64_t ks = pow2_floor(bytes / 32768 > 0 ? bytes / 32768 : 1);
         const int64_t max_ks = m / 128 < 32 ? m / 128 : 32;  // each wave keeps at least one step
         while (ks > max_ks) ks /= 2;
         pl.ks = r > 0 ? (int)ks : 1;
