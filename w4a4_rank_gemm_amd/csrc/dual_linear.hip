@@ -6,12 +6,13 @@
 // the residual partial sums and the low-rank product live only in registers and
 // are merged in one epilogue that stores fp16 once.
 //
-// Two main loops share one epilogue: dual_linear_decode for few tokens (HBM-bound,
-// operands straight from global memory) and dual_linear_pf for many tokens
-// (matrix-core-bound, operands staged through an LDS ring). Both expand packed
-// int4 codes to int8 (x16, see unpack16) and issue v_mfma_i32_16x16x64_i8 --
-// gfx950 has no int4 matrix instruction. The accumulator holds 256 * acc exactly
-// (|acc| <= 49 m, m <= 131072).
+// Two main loops with the same epilogue arithmetic: dual_linear_decode for few tokens
+// (HBM-bound, operands straight from global memory) and dual_linear_pf for many tokens
+// (matrix-core-bound, operands staged through an LDS ring). Both expand packed int4
+// codes to int8 (x16, see unpack16) and issue v_mfma_i32_16x16x64_i8 -- gfx950 has no
+// int4 matrix instruction. The accumulator holds 256 * acc exactly (|acc| <= 49 m,
+// m <= 131072). Both also run the group-wise (GRP) and W4A8 (A8) variants described
+// at each kernel.
 //
 // Epilogue: acc is dequantized in place to fp32, then used as the C operand of
 // v_mfma_f32_16x16x32_f16 over the rank dimension with A = L2^T rows and
@@ -57,7 +58,8 @@ __device__ __forceinline__ v4i lr4_tile(const DualArgs &a, int64_t ch_row, int64
 // valid row and their outputs never stored -- so nothing serialises them, and the
 // low-rank operands of the epilogue are loaded first so their latency hides under
 // the main loop.
-// T partial-sum slices the decode epilogue adds itself, per 32-rank step it loads
+// Most partial sums of T (K slices x 32-rank steps) one lane of a decode epilogue
+// holds; a shape with more slices gets T reduced first.
 constexpr int kMaxTSlices = 16;
 
 // Group-wise scales (GRP, groups of kGroup = 128 along K): one 64-byte piece of a
@@ -353,8 +355,8 @@ static hipError_t launch_decode(const DualArgs &a, hipStream_t stream) {
 // ---------------------------------------------------------------------------------
 // Many tokens: the main loop is bound by the int8 matrix cores. A CTA owns a BN x BM
 // tile of Y^T (BN output channels by BM tokens) and streams K in stages of 128 codes
-// (64 bytes per row) through a ring of S stages in LDS, filled by direct global ->
-// LDS loads (global_load_lds_dwordx4: no register staging, S - 1 stages in flight).
+// (64 bytes per row) through a ring of S stages in LDS, filled by direct-to-LDS buffer
+// loads (no register staging, S - 1 stages in flight).
 // A stage holds the 128-code K slice of the tile's BN weight rows and BM token rows
 // (64 bytes per row) as 1 KB blocks of 16 rows. Inside a block, rows 2s and 2s + 1
 // share the 128-byte line s (s = 0..7): the 16-byte chunk c of row 2s + h has logical
@@ -381,11 +383,9 @@ __host__ __device__ __forceinline__ int64_t xcd_order(int64_t bid, int64_t ntile
     return x * q + (x < rem ? x : rem) + j;
 }
 
-// Epilogue of the many-token kernels for a wave's FN x FM tiles of 16 x 16, the wave
-// at (wn, wm) of a BN x BM CTA tile at (ch0, tok0): dequantize, add the low-rank
-// branch, store fp16 (or the exact integer sum).
-// Second half of the many-token epilogue, from the dequantized residual y: add the
-// low-rank branch and store fp16.
+// Second half of the many-token epilogue, from the dequantized residual y of a wave's
+// FN x FM tiles of 16 x 16 (the wave at (wn, wm) of a BN x BM CTA tile at (ch0, tok0)):
+// add the low-rank branch and store fp16.
 template <int BN, int BM, int WN, int WM, bool LR4, int FN, int FM>
 __device__ __forceinline__ void pf_finish(const DualArgs &a, v4f (&y)[FN][FM], int64_t ch0, int64_t tok0, int wn, int wm,
                                           int li, int g) {
@@ -442,7 +442,9 @@ __device__ __forceinline__ void pf_finish(const DualArgs &a, v4f (&y)[FN][FM], i
         }
 }
 
-// SH: log2 of the operands' combined scale in acc (8 for 4-bit x 4-bit, 4 for W4A8)
+// Epilogue of the many-token kernels: dequantize the integer sums, then pf_finish (or
+// store the exact integer sums). SH: log2 of the operands' combined scale in acc (8 for
+// 4-bit x 4-bit, 4 for W4A8).
 template <int BN, int BM, int WN, int WM, bool STORE_ACC, bool LR4, int SH, int FN, int FM>
 __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM], int64_t ch0, int64_t tok0, int wn, int wm,
                                             int li, int g) {
