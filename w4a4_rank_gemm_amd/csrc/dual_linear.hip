@@ -229,6 +229,34 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
         mma(bw, bx, sw4, sx1);
     }
 
+    // Without the prefetch above (a wave owns several epilogue tiles), the low-rank
+    // operands of all of the wave's tiles are loaded here, after the main loop and
+    // before the reduction, so they arrive together and under the barrier (tile
+    // indices past the last tile reload the last one, unused).
+    constexpr int TPW = (TILES + NW - 1) / NW;  // epilogue tiles per wave
+    constexpr bool LATE = !STORE_ACC && !PREFETCH && RS > 0 && TPW * RS <= 8;  // else: per tile, below
+    v8h lal[LATE ? TPW : 1][LATE ? RS : 1];
+    float4 tal[LATE ? TPW : 1][LATE ? RS : 1], tbl[LATE ? TPW : 1][LATE ? RS : 1];
+    if constexpr (LATE) {
+        if (!a.lr4) {
+#pragma unroll
+            for (int e = 0; e < TPW; ++e) {
+                const int tile = wave + e * NW < TILES ? wave + e * NW : TILES - 1;
+                const int64_t chr = ch0 + (tile / FM) * 16 + li, tokr = (tile % FM) * 16 + li;
+                const uint16_t *l2row = a.l2t + (chr < a.n ? chr : a.n - 1) * a.r;
+                const float *trow = a.t + (tokr < a.b ? tokr : a.b - 1) * a.r;
+#pragma unroll
+                for (int s = 0; s < RS; ++s) {
+                    const int rank = s * 32 + g * 8;
+                    const int rk = rank < a.r ? rank : 0;
+                    lal[e][s] = load_h8(l2row + rk);
+                    tal[e][s] = *reinterpret_cast<const float4 *>(trow + rk);
+                    tbl[e][s] = *reinterpret_cast<const float4 *>(trow + rk + 4);
+                }
+            }
+        }
+    }
+
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -239,7 +267,10 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
                 red[wave][fn * FM + fm][lane] = acc[fn][fm];
         }
     __syncthreads();
-    for (int tile = wave; tile < TILES; tile += NW) {
+#pragma unroll
+    for (int e = 0; e < TPW; ++e) {
+        const int tile = wave + e * NW;
+        if (tile >= TILES) break;
         const int fn_e = tile / FM, fm_e = tile % FM;
         v4i sum = red[0][tile][lane];
         v4f ysum = __builtin_bit_cast(v4f, red[0][tile][lane]);
@@ -286,6 +317,10 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
                         }
                     y = mfma_f16(l2f[s], live ? f32x8_to_h8(t0, t1) : v8h{}, y);
                 }
+            } else if constexpr (LATE) {
+#pragma unroll
+                for (int s = 0; s < RS; ++s)
+                    y = mfma_f16(lal[e][s], s * 32 + g * 8 < a.r ? f32x8_to_h8(tal[e][s], tbl[e][s]) : v8h{}, y);
             } else if constexpr (RS > 0) {
                 // every rank step's L2^T and T pieces are loaded before the first is used
                 const int64_t chr = ch0 + fn_e * 16 + li, tokr = fm_e * 16 + li;
