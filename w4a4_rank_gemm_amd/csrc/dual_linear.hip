@@ -516,9 +516,9 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 }
 
 // Three CTAs per compute unit (12 waves) fit the LDS ring; the register budget that
-// allows is asked for explicitly (measured 7-11% faster than two CTAs on the prefill
-// shapes). The group-wise variant (GRP) keeps a second, fp32 set of accumulators and
-// runs two CTAs per unit.
+// allows is asked for explicitly (measured 7-12% faster than two CTAs on the prefill
+// shapes, the group-wise variant (GRP) included, which keeps a second, fp32 set of
+// accumulators). W4A8's 24 KB stages leave room for two CTAs per unit.
 //
 // GRP (groups of kGroup = 128 along K): a stage is one group. Each slot of the ring
 // also holds the stage's scales, s_W of the tile's BN channels and s_X of its BM tokens
@@ -534,7 +534,7 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 // (perm16); the accumulator holds 16 acc.
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false,
           bool A8 = false>
-__global__ __launch_bounds__(WN * WM * 64, GRP || A8 ? 2 : 3)
+__global__ __launch_bounds__(WN * WM * 64, A8 ? 2 : 3)
 void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     constexpr int NT = WN * WM * 64;
     constexpr int FN = BN / (16 * WN), FM = BM / (16 * WM);
