@@ -518,7 +518,8 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 // Three CTAs per compute unit (12 waves) fit the LDS ring; the register budget that
 // allows is asked for explicitly (measured 7-12% faster than two CTAs on the prefill
 // shapes, the group-wise variant (GRP) included, which keeps a second, fp32 set of
-// accumulators). W4A8's 24 KB stages leave room for two CTAs per unit.
+// accumulators). W4A8's stages are 24 KB, so it runs a two-stage ring (one stage in
+// flight) to fit three CTAs per unit: 2-10% faster than three stages at two CTAs.
 //
 // GRP (groups of kGroup = 128 along K): a stage is one group. Each slot of the ring
 // also holds the stage's scales, s_W of the tile's BN channels and s_X of its BM tokens
@@ -534,7 +535,7 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 // (perm16); the accumulator holds 16 acc.
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false,
           bool A8 = false>
-__global__ __launch_bounds__(WN * WM * 64, A8 ? 2 : 3)
+__global__ __launch_bounds__(WN * WM * 64, A8 && S > 2 ? 2 : 3)
 void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     constexpr int NT = WN * WM * 64;
     constexpr int FN = BN / (16 * WN), FM = BM / (16 * WM);
@@ -732,11 +733,11 @@ template <int BN, int BM, int WN, int WM, int S, int GM, int RB>
 static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
     const int64_t tiles_n = (a.n + BN - 1) / BN, tiles_m = (a.b + BM - 1) / BM;
     const dim3 grid((unsigned)(tiles_n * tiles_m)), block(WN * WM * 64);
-    if (a.a8 && a.acc)
-        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, true, false, false, true>), grid, block, 0, stream, a,
+    if (a.a8 && a.acc)  // W4A8: two stages (see dual_linear_pf)
+        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, 2, GM, RB, true, false, false, true>), grid, block, 0, stream, a,
                            (int)tiles_n, (int)tiles_m);
     else if (a.a8)
-        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, false, false, false, true>), grid, block, 0, stream, a,
+        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, 2, GM, RB, false, false, false, true>), grid, block, 0, stream, a,
                            (int)tiles_n, (int)tiles_m);
     else if (a.acc)
         hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, true>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
