@@ -520,6 +520,9 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 // shapes, the group-wise variant (GRP) included, which keeps a second, fp32 set of
 // accumulators). W4A8's stages are 24 KB, so it runs a two-stage ring (one stage in
 // flight) to fit three CTAs per unit: 2-10% faster than three stages at two CTAs.
+// The per-token W4A4 kernel on a two-stage ring fits four CTAs per unit (128 registers,
+// a few spilled around the epilogue only); launch_pf takes it where the grid fills all
+// four slots of every unit at least once (see there).
 //
 // GRP (groups of kGroup = 128 along K): a stage is one group. Each slot of the ring
 // also holds the stage's scales, s_W of the tile's BN channels and s_X of its BM tokens
@@ -535,7 +538,7 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 // (perm16); the accumulator holds 16 acc.
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false,
           bool A8 = false>
-__global__ __launch_bounds__(WN * WM * 64, A8 && S > 2 ? 2 : 3)
+__global__ __launch_bounds__(WN * WM * 64, A8 ? (S > 2 ? 2 : 3) : (S == 2 ? 4 : 3))
 void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     constexpr int NT = WN * WM * 64;
     constexpr int FN = BN / (16 * WN), FM = BM / (16 * WM);
@@ -729,26 +732,36 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
         pf_epilogue<BN, BM, WN, WM, STORE_ACC, LR4, A8 ? 4 : 8>(a, acc, ch0, tok0, wn, wm, li, g);
 }
 
-template <int BN, int BM, int WN, int WM, int S, int GM, int RB>
-static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
+template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false,
+          bool A8 = false>
+static hipError_t launch_pf_kernel(const DualArgs &a, hipStream_t stream) {
     const int64_t tiles_n = (a.n + BN - 1) / BN, tiles_m = (a.b + BM - 1) / BM;
-    const dim3 grid((unsigned)(tiles_n * tiles_m)), block(WN * WM * 64);
-    if (a.a8 && a.acc)  // W4A8: two stages (see dual_linear_pf)
-        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, 2, GM, RB, true, false, false, true>), grid, block, 0, stream, a,
-                           (int)tiles_n, (int)tiles_m);
-    else if (a.a8)
-        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, 2, GM, RB, false, false, false, true>), grid, block, 0, stream, a,
-                           (int)tiles_n, (int)tiles_m);
-    else if (a.acc)
-        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, true>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
-    else if (a.group)
-        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, false, false, true>), grid, block, 0, stream, a, (int)tiles_n,
-                           (int)tiles_m);
-    else if (a.lr4)
-        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, false, true>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
-    else
-        hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, false>), grid, block, 0, stream, a, (int)tiles_n, (int)tiles_m);
+    hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, STORE_ACC, LR4, GRP, A8>), dim3((unsigned)(tiles_n * tiles_m)),
+                       dim3(WN * WM * 64), 0, stream, a, (int)tiles_n, (int)tiles_m);
     return hipGetLastError();
+}
+
+// Many tokens: 128 x 128 tiles, XCD groups of 8 token tiles (the fastest exact variant
+// measured on MI355X for the gate/up and down shapes). The per-token W4A4 kernel runs a
+// two-stage ring at four CTAs per compute unit once the grid has at least 4 x 256 tiles,
+// and a three-stage ring at three CTAs below that, where the fourth slots would stay
+// partly empty and the deeper ring hides more latency (measured: 3-5% faster above, 1-5%
+// slower below, on 13 prefill shapes). The debug accumulator path follows the same rule,
+// so it checks the main loop that the same shape runs for Y.
+static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
+    constexpr int BN = 128, BM = 128, WN = 2, WM = 2, GM = 8, RB = 64;
+    const int64_t tiles = ((a.n + BN - 1) / BN) * ((a.b + BM - 1) / BM);
+    const bool four = tiles >= 4 * 256;
+    if (a.a8)  // W4A8: two stages (see dual_linear_pf)
+        return a.acc ? launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, true, false, false, true>(a, stream)
+                     : launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, false, false, false, true>(a, stream);
+    if (a.acc)
+        return four ? launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, true>(a, stream)
+                    : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, true>(a, stream);
+    if (a.group) return launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, false, true>(a, stream);
+    if (a.lr4) return launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, true>(a, stream);
+    return four ? launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, false>(a, stream)
+                : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false>(a, stream);
 }
 
 // Decode tiles (FN x FM blocks of 16 channels x 16 tokens per CTA): wider channel
@@ -768,9 +781,7 @@ hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream) {
     if (a.b <= 16) return a.n >= 16384 ? launch_decode<2, 1, 8>(a, stream) : launch_decode<1, 1, 8>(a, stream);
     if (a.b <= 32) return a.n >= 8192 ? launch_decode<4, 2, 2>(a, stream) : launch_decode<1, 2, 4>(a, stream);
     if (a.b <= 64) return a.n >= 8192 ? launch_decode<2, 4, 2>(a, stream) : launch_decode<1, 4, 4>(a, stream);
-    // many tokens: 128 x 128 tiles, 3-stage LDS ring, XCD groups of 8 token tiles
-    // (the fastest exact variant measured on MI355X for the gate/up and down shapes)
-    return launch_pf<128, 128, 2, 2, 3, 8, 64>(a, stream);
+    return launch_pf(a, stream);
 }
 
 int dual_max_t_slices(int64_t b, int64_t n, int r) {
