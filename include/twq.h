@@ -35,7 +35,15 @@
  *  - X: fp16 [b][m], row-major (one token per row). Y: fp16 [b][n].
  *  - Packed 4-bit codes: two per byte, K-contiguous rows; byte t of a row holds
  *    code 2t in its low nibble and code 2t+1 in its high nibble, each a 4-bit
- *    two's complement value in [-7, 7].
+ *    two's complement value in [-7, 7]. Q_X (and the low-rank codes) are stored
+ *    row by row, m/2 bytes a row.
+ *  - Q_W is stored in 16-channel panels, n m / 2 bytes in all: channels
+ *    16p .. 16p+15 form panel p (panels in channel order); a panel holds its m/128
+ *    pieces in K order, and a piece holds bytes 64c .. 64c+63 of each of the 16
+ *    channels' rows, in channel order. Byte t of channel j's row is at offset
+ *    ((j / 16) (m / 128) + t / 64) 1024 + (j % 16) 64 + t % 64. A 16-channel x
+ *    128-code matrix operand is then 1 KB of contiguous memory. twq_pack_weight
+ *    writes this layout; every entry point that takes qw reads it.
  *  - Scales are fp32: s_X one per token, s_W one per output channel.
  *  - Quantization reading of eq. (1): s = fl32(max|v| / 7), q = round-half-even
  *    (fl32(v / s)) with correctly rounded binary32 divisions; an all-zero
@@ -98,7 +106,7 @@ twq_status twq_quantize_act(const void *x, int64_t b, int64_t m, void *qx, float
  *
  *   w_res f32 [n][m]                   residual weight, one row per output channel
  *                                      (the transpose of the pages' m x n W)
- *   qw    u8  [n][m/2]    (out)        packed 4-bit codes Q_W
+ *   qw    u8  n m / 2     (out)        packed 4-bit codes Q_W, in panels (above)
  *   sw    f32 [n]         (out)        per-channel scales s_W
  */
 twq_status twq_pack_weight(const float *w_res, int64_t n, int64_t m, void *qw, float *sw,
@@ -229,7 +237,8 @@ twq_status twq_debug_residual_acc_a8(const void *qx, const void *qw, int32_t *ac
 
 /*
  *   l1t   fp16 [r][m], l2t fp16 [n][r]   as for twq_quantize_act / twq_dual_linear
- *   ql1   u8  [r][m/2]  (out)            codes of L1 per rank t (row t = column t of L1)
+ *   ql1   u8  r m / 2   (out)            codes of L1 per rank t (row t = column t of L1),
+ *                                        in the panel layout of Q_W (r output channels of H)
  *   sl1   f32 [r]       (out)            s_L1[t] = max_k |L1[k][t]| / 7
  *   ql2   u8  [n][r/2]  (out)            codes of L2, K = r contiguous per output channel
  *   sl2   f32 [r]       (out)            s_L2[t] = max_j |L2[t][j]| / 7

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import w4a4_rank_gemm_amd as twq
@@ -163,3 +164,18 @@ def test_a8_validation():
     assert need8 >= need4 + 16 * 4096 // 2 - 255  # one byte per activation code instead of half a byte
     assert L.twq_linear_a8(A, A, A, A, A, 32, A, 16, 4096, 4096, A, need8 - 1, None) == WORKSPACE
     assert L.twq_linear_a8(None, None, None, None, None, 32, None, 0, 4096, 4096, None, 0, None) == OK
+
+
+def test_panel_layout_helpers_follow_the_documented_offsets():
+    """tests/panels.py against the offset formula of twq.h, by an explicit loop:
+    byte t of channel j at ((j / 16)(m / 128) + t / 64) 1024 + (j % 16) 64 + t % 64."""
+    from tests.panels import from_panels, to_panels
+    rng = np.random.default_rng(7)
+    n, m = 48, 384
+    rows = rng.integers(0, 256, (n, m // 2), dtype=np.uint8)
+    flat = np.zeros(n * m // 2, np.uint8)
+    for j in range(n):
+        for t in range(m // 2):
+            flat[((j // 16) * (m // 128) + t // 64) * 1024 + (j % 16) * 64 + t % 64] = rows[j, t]
+    assert np.array_equal(to_panels(rows).reshape(-1), flat)
+    assert np.array_equal(from_panels(to_panels(rows)), rows)

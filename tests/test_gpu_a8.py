@@ -14,6 +14,7 @@ import torch
 import oracle
 import synth
 import w4a4_rank_gemm_amd as twq
+from tests.panels import to_panels
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +70,7 @@ def test_a8_matches_oracle(b, m, n, r):
     ref = oracle.dual_linear_a8(d["x"], d["w_res"], d["l1t"], d["l2t"])
     assert np.array_equal(_np(g["qx"]), ref["qx"]), "Q_X codes"
     assert np.array_equal(_np(g["sx"]), ref["sx"]), "s_X"
-    assert np.array_equal(_np(g["qw"]), ref["qw_packed"]) and np.array_equal(_np(g["sw"]), ref["sw"])
+    assert np.array_equal(_np(g["qw"]), to_panels(ref["qw_packed"])) and np.array_equal(_np(g["sw"]), ref["sw"])
     assert np.array_equal(_np(g["acc"]).astype(np.int64), ref["acc"]), "int32 accumulator"
     err, scale = check_y(_np(g["y"]), ref["y"])
     assert torch.equal(g["y1"], g["y"]), "twq_linear_a8 differs from the split calls"

@@ -14,6 +14,7 @@ import torch
 import oracle
 import synth
 import w4a4_rank_gemm_amd as twq
+from tests.panels import to_panels
 from tests.test_gpu_quant_ties import _row
 
 pytestmark = pytest.mark.gpu
@@ -51,7 +52,7 @@ def check_codes(d, g):
     assert np.array_equal(_np(g["qx"]), qxp), "Q_X bytes"
     assert np.array_equal(_np(g["sx"]), sx.T), "s_X"
     _, qwp, sw = oracle.quantize_weight_grouped(d["w_res"], G)
-    assert np.array_equal(_np(g["qw"]), qwp), "Q_W bytes"
+    assert np.array_equal(_np(g["qw"]), to_panels(qwp)), "Q_W bytes"
     assert np.array_equal(_np(g["sw"]), sw.T), "s_W"
     assert torch.equal(g["y1"], g["y"]), "twq_linear_grouped differs from the split calls"
 

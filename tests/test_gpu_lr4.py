@@ -14,6 +14,7 @@ import torch
 import oracle
 import synth
 import w4a4_rank_gemm_amd as twq
+from tests.panels import from_panels, to_panels
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +51,8 @@ def check_factors(d, g):
     ref = oracle.quantize_lowrank(d["l1t"], d["l2t"])
     for k in ("ql1_packed", "sl1", "ql2_packed", "sl2", "c"):
         gk = k.replace("_packed", "")
-        assert np.array_equal(_np(g["f"][gk]), ref[k]), k
+        want = to_panels(ref[k]) if k == "ql1_packed" else ref[k]  # Q_L1 is H's weight operand
+        assert np.array_equal(_np(g["f"][gk]), want), k
     return ref
 
 
@@ -68,7 +70,7 @@ def test_lr4_hand_worked_padded():
     l2t = np.zeros((16, 32), np.float16)
     l2t[:2, :2] = np.array(gld["l2t"])
     g = run_lr4({"x": x, "w_res": w, "l1t": l1t, "l2t": l2t})
-    ql1 = oracle.unpack_codes(_np(g["f"]["ql1"]))
+    ql1 = oracle.unpack_codes(from_panels(_np(g["f"]["ql1"])))
     assert ql1[:2, :4].tolist() == gld["ql1"] and (ql1[2:] == 0).all()
     ql2 = oracle.unpack_codes(_np(g["f"]["ql2"]))
     assert ql2[:2, :2].tolist() == gld["ql2"] and (ql2[:, 2:] == 0).all()

@@ -15,6 +15,7 @@ import torch
 import oracle
 import synth
 import w4a4_rank_gemm_amd as twq
+from tests.panels import to_panels, from_panels
 
 pytestmark = pytest.mark.gpu
 
@@ -67,7 +68,7 @@ def check_full(d, g):
     ref = oracle.dual_linear(d["x"], d["w_res"], d["l1t"], d["l2t"])
     assert np.array_equal(_np(g["qx"]), ref["qx_packed"]), "Q_X bytes"
     assert np.array_equal(_np(g["sx"]), ref["sx"]), "s_X"
-    assert np.array_equal(_np(g["qw"]), ref["qw_packed"]), "Q_W bytes"
+    assert np.array_equal(_np(g["qw"]), to_panels(ref["qw_packed"])), "Q_W bytes"
     assert np.array_equal(_np(g["sw"]), ref["sw"]), "s_W"
     if g["acc"] is not None:
         assert np.array_equal(_np(g["acc"]).astype(np.int64), ref["acc"]), "int32 accumulator"
@@ -101,7 +102,7 @@ def test_e6_hand_worked_layer_padded():
     assert qx[:, :4].tolist() == g["qx"] and (qx[:, 4:] == 0).all()
     assert _np(out["qx"])[:, :2].tolist() == g["qx_packed"]
     assert _np(out["sx"]).astype(np.float64).tolist() == g["sx"]
-    qw = oracle.unpack_codes(_np(out["qw"]))
+    qw = oracle.unpack_codes(from_panels(_np(out["qw"])))
     assert qw[:3, :4].tolist() == g["qw"] and (qw[3:] == 0).all()
     assert _np(out["sw"])[:3].astype(np.float64).tolist() == g["sw"]
     assert _np(out["acc"])[:, :3].tolist() == g["acc"]
@@ -214,7 +215,7 @@ def test_config_full_size_sampled(name):
     qx_ref, qxp_ref, sx_ref = oracle.quantize_act(d["x"])
     assert np.array_equal(_np(g["qx"]), qxp_ref) and np.array_equal(_np(g["sx"]), sx_ref)
     _, qwp_ref, sw_ref = oracle.quantize_weight(d["w_res"])
-    assert np.array_equal(_np(g["qw"]), qwp_ref) and np.array_equal(_np(g["sw"]), sw_ref)
+    assert np.array_equal(_np(g["qw"]), to_panels(qwp_ref)) and np.array_equal(_np(g["sw"]), sw_ref)
     rng = synth.rng_for(100 + b)
     rows = rng.integers(0, b, 384)
     cols = rng.integers(0, n, 384)

@@ -175,7 +175,10 @@ def quantize_act(x: torch.Tensor, l1t: torch.Tensor | None = None):
 
 
 def pack_weight(w_res: torch.Tensor):
-    """W_res f32 [n][m] -> (Q_W u8 [n][m/2], s_W f32 [n])."""
+    """W_res f32 [n][m] -> (Q_W u8 [n][m/2], s_W f32 [n]).
+
+    Q_W's n*m/2 bytes are in the library's 16-channel panel layout (twq.h), not one
+    channel per row: the tensor's shape only records n and m."""
     _need(w_res, "w_res", torch.float32, 2)
     n, m = w_res.shape
     dev = w_res.device
@@ -273,7 +276,7 @@ def quantize_act_grouped(x: torch.Tensor, l1t: torch.Tensor | None = None, g: in
 
 
 def pack_weight_grouped(w_res: torch.Tensor, g: int = GROUP):
-    """W_res f32 [n][m] -> (Q_W u8 [n][m/2], s_W f32 [m/g][n])."""
+    """W_res f32 [n][m] -> (Q_W u8 [n][m/2] in the panel layout, s_W f32 [m/g][n])."""
     _need(w_res, "w_res", torch.float32, 2)
     n, m = w_res.shape
     dev = w_res.device
@@ -443,7 +446,9 @@ def debug_residual_acc(qx, qw):
 
 
 def pack_lowrank_int4(l1t: torch.Tensor, l2t: torch.Tensor):
-    """fp16 L1^T [r][m], L2^T [n][r] -> dict ql1 [r][m/2], sl1 [r], ql2 [n][r/2], sl2 [r], c [r]."""
+    """fp16 L1^T [r][m], L2^T [n][r] -> dict ql1 [r][m/2], sl1 [r], ql2 [n][r/2], sl2 [r], c [r].
+
+    ql1 is in the panel layout of pack_weight (it is the weight operand of H = Q_X Q_L1^T)."""
     _need(l1t, "l1t", torch.float16, 2)
     _need(l2t, "l2t", torch.float16, 2)
     r, m = l1t.shape

@@ -53,7 +53,8 @@ __device__ __forceinline__ v4i lr4_tile(const DualArgs &a, int64_t ch_row, int64
 // Few tokens (b <= 64): the layer streams Q_W once from HBM and little else. A CTA
 // owns FN*16 output channels and all tokens (FM tiles of 16); its NW waves split
 // K and feed the matrix cores straight from global memory, U 16-byte loads per
-// operand row issued before any is consumed; the NW partial accumulators are
+// operand row issued before any is consumed (a weight operand is one contiguous 1 KB
+// piece of a panel, so each wave streams FN contiguous runs); the NW partial accumulators are
 // added through LDS. Loads are unconditional -- rows past n or b are clamped to a
 // valid row and their outputs never stored -- so nothing serialises them, and the
 // low-rank operands of the epilogue are loaded first so their latency hides under
@@ -85,11 +86,13 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
     const int64_t nch = a.m / 128;  // 64-byte pieces of a packed row
     const int64_t cb = wave * nch / NW, ce = (wave + 1) * nch / NW;
 
+    // this lane's 16 bytes of piece c of channel tile fn: wrow[fn] + c kPanelPiece (a
+    // piece of a panel is one contiguous 1 KB operand block)
     const uint8_t *wrow[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
         const int64_t ch = ch0 + fn * 16 + li;
-        wrow[fn] = a.qw + (ch < a.n ? ch : a.n - 1) * kb + g * 16;
+        wrow[fn] = a.qw + qw_offset(ch < a.n ? ch : a.n - 1, (int64_t)g * 16 + cb * kPieceBytes, a.m);
     }
     const uint8_t *xrow[FM];
 #pragma unroll
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) bw[u][fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (c + u) * 64);
+            for (int fn = 0; fn < FN; ++fn) bw[u][fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (c - cb + u) * kPanelPiece);
             load_x(c + u, bx[u]);
             load_scales(c + u, sw4[u], sx1[u]);
         }
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
         float4 sw4[GRP ? FN : 1];
         float sx1[GRP ? FM : 1];
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) bw[fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + c * 64);
+        for (int fn = 0; fn < FN; ++fn) bw[fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (c - cb) * kPanelPiece);
         load_x(c, bx);
         load_scales(c, sw4, sx1);
         mma(bw, bx, sw4, sx1);
@@ -350,41 +353,54 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
     }
 }
 
-template <int FN, int FM, int U, int RS>
+// A 512-thread CTA gives a wave at most 256 registers. The variants that hold more --
+// T's partial sums prefetched for a CTA of several tiles, the group-wise fp32 sums --
+// run four waves instead, each over twice the K range with twice the pieces in flight
+// (U4); every instantiation then fits without spilling. W4A8 token rows and group-wise
+// scales take registers too, so those variants have half the pieces in flight (halved).
+constexpr int halved(int u) { return u > 4 ? u / 2 : u; }
+template <int FN, int FM, int U, int NW, int RS>
 static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.n + FN * 16 - 1) / (FN * 16)));
     constexpr int TK = RS > 0 && FN * FM <= 4 ? kMaxTSlices / RS : 1;  // partial sums of T the epilogue adds
-    constexpr int UG = U > 4 ? U / 2 : U;
-    if (a.a8) {  // W4A8: twice the token bytes per piece, so half the pieces in flight
+    constexpr int U4 = NW == 8 ? (2 * U < 8 ? 2 * U : 8) : U;
+    constexpr bool FIT = FN * FM == 1;  // one tile: its prefetched partial sums fit eight waves
+    constexpr int NWT = FIT ? NW : 4, UT = FIT ? U : U4;                      // T as partial sums
+    constexpr int NWA = RS >= 8 && FN * FM >= 8 ? 4 : NW, UA = NWA == NW ? U : U4;  // W4A8, T whole
+    const dim3 grid((unsigned)((a.n + FN * 16 - 1) / (FN * 16)));
+    const bool tk = TK > 1 && a.tks > 1;
+    if (a.a8) {
         if (a.acc)
-            hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, 0, true, 1, 4, false, true>), grid, dim3(256), 0, stream, a);
-        else if (TK > 1 && a.tks > 1)
-            hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, TK, 4, false, true>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((dual_linear_decode<FN, FM, halved(U), 0, true, 1, NW, false, true>), grid, dim3(NW * 64), 0,
+                               stream, a);
+        else if (tk)
+            hipLaunchKernelGGL((dual_linear_decode<FN, FM, halved(UT), RS, false, TK, NWT, false, true>), grid,
+                               dim3(NWT * 64), 0, stream, a);
         else
-            hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, 1, 4, false, true>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((dual_linear_decode<FN, FM, halved(UA), RS, false, 1, NWA, false, true>), grid,
+                               dim3(NWA * 64), 0, stream, a);
         return hipGetLastError();
     }
     if (a.acc)
-        hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true>), grid, dim3(256), 0, stream, a);
-    else if (a.group && TK > 1 && a.tks > 1)  // group-wise: half the pieces in flight, which leaves room for their scales
-        hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, TK, 4, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true, 1, NW>), grid, dim3(NW * 64), 0, stream, a);
+    else if (a.group && tk)
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, halved(U4), RS, false, TK, 4, true>), grid, dim3(256), 0, stream, a);
     else if (a.group)
-        hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, 1, 4, true>), grid, dim3(256), 0, stream, a);
-    else if (TK > 1 && a.tks > 1)
-        hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false, TK>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, halved(U4), RS, false, 1, 4, true>), grid, dim3(256), 0, stream, a);
+    else if (tk)
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, UT, RS, false, TK, NWT>), grid, dim3(NWT * 64), 0, stream, a);
     else
-        hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false, 1, NW>), grid, dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int FN, int FM, int U>
+template <int FN, int FM, int U, int NW>
 static hipError_t launch_decode(const DualArgs &a, hipStream_t stream) {
     // rank steps of 32 the epilogue prefetches
-    if (a.r == 0) return launch_decode_rs<FN, FM, U, 0>(a, stream);
-    if (a.r <= 32) return launch_decode_rs<FN, FM, U, 1>(a, stream);
-    if (a.r <= 64) return launch_decode_rs<FN, FM, U, 2>(a, stream);
-    if (a.r <= 128) return launch_decode_rs<FN, FM, U, 4>(a, stream);
-    return launch_decode_rs<FN, FM, U, 8>(a, stream);
+    if (a.r == 0) return launch_decode_rs<FN, FM, U, NW, 0>(a, stream);
+    if (a.r <= 32) return launch_decode_rs<FN, FM, U, NW, 1>(a, stream);
+    if (a.r <= 64) return launch_decode_rs<FN, FM, U, NW, 2>(a, stream);
+    if (a.r <= 128) return launch_decode_rs<FN, FM, U, NW, 4>(a, stream);
+    return launch_decode_rs<FN, FM, U, NW, 8>(a, stream);
 }
 
 // ---------------------------------------------------------------------------------
@@ -575,7 +591,8 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     // this thread's DMA sources: slot q = j * NT + tid of each stage is 16-byte position
     // q % 8 of 128-byte line (q % (16 CPR)) / 8 of block q / (16 CPR). Each j lies wholly
     // in the weight rows or wholly in the token rows, so its address is a uniform tile
-    // base (advanced by RB bytes per stage) plus a 32-bit per-lane offset.
+    // base plus a 32-bit per-lane offset, advanced per stage by RB bytes in a token row
+    // and by 16 RB bytes in the weight panels (a stage is RB / 64 pieces of each panel).
     static_assert(NT % 64 == 0 && (BN * CPR) % NT == 0, "each DMA group in one operand");
     const int64_t xb = A8 ? a.m : kb;           // bytes per token row
     const uint8_t *wbase = a.qw + ch0 * kb, *xbase = a.qx + tok0 * xb;
@@ -595,7 +612,7 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
             rel = (tok < a.b ? tok : a.b - 1) - tok0;
         }
         // A8: token rows BN + h BM + t hold bytes 64 h .. 64 h + 63 of token t's slice
-        off[j] = (uint32_t)(row < BN ? rel * kb + chunk * 16 : rel * xb + ((row - BN) / BM) * 64 + chunk * 16);
+        off[j] = (uint32_t)(row < BN ? qw_offset(rel, chunk * 16, a.m) : rel * xb + ((row - BN) / BM) * 64 + chunk * 16);
     }
     __shared__ __attribute__((aligned(16))) uint8_t ring[S * SLOT];
     // GRP: this thread's scale: waves 0-1 load s_W of channel ch0 + tid, waves 2-3 s_X of
@@ -618,7 +635,7 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
         for (int j = 0; j < DPT; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds((j * NT) / CPR < BN ? rw : rx,
                                                      (__attribute__((address_space(3))) void *)(dst + (j * NT + wave * kWave) * 16),
-                                                     16, (int)off[j], st * RB * ((j * NT) / CPR < BN ? 1 : XH), 0, 0);
+                                                     16, (int)off[j], st * RB * ((j * NT) / CPR < BN ? kPanelRows : XH), 0, 0);
         if constexpr (GRP) {
             // group st's row of the group-major scales, from the tile's first channel or token
             const float *sb = wave_u < BN / kWave ? a.sw + (int64_t)st * a.n + ch0 : a.sx + (int64_t)st * a.b + tok0;
@@ -764,24 +781,35 @@ static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
                 : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false>(a, stream);
 }
 
-// Decode tiles (FN x FM blocks of 16 channels x 16 tokens per CTA): wider channel
-// tiles read Q_X fewer times, as long as the grid still covers the chip (measured on
-// MI355X with HIP graphs, weights cold). false: many tokens, the LDS-ring kernel.
-// launch_dual_linear dispatches on the same conditions.
+// Decode tiles (FN x FM blocks of 16 channels x 16 tokens per CTA, FM = ceil(b / 16)):
+// the widest channel tile that still leaves at least 192 CTAs, at most 2 blocks for 16
+// tokens, 8 for 32 and 4 for 64. Wider tiles read Q_X from L2 fewer times; fewer CTAs
+// than that leave compute units idle. Measured on MI355X over 20 few-token shapes
+// (m, n from 4096 to 28672; weights cold): within 4% of the best of 6 tilings on each.
+// false: many tokens, the LDS-ring kernel.
 static bool decode_shape(int64_t b, int64_t n, int &fn, int &fm) {
-    if (b <= 16) { fn = n >= 16384 ? 2 : 1; fm = 1; return true; }
-    if (b <= 32) { fn = n >= 8192 ? 4 : 1; fm = 2; return true; }
-    if (b <= 64) { fn = n >= 8192 ? 2 : 1; fm = 4; return true; }
-    return false;
+    if (b > 64) return false;
+    fm = b <= 16 ? 1 : b <= 32 ? 2 : 4;
+    const int cap = b <= 16 ? 2 : b <= 32 ? 8 : 4;
+    for (fn = 1; fn < cap && n / (32 * fn) >= 192; fn *= 2) {}
+    return true;
 }
 
 hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream) {
     if (a.b == 0 || a.n == 0) return hipSuccess;
     if (a.tks > 1 && (a.acc || a.lr4 || a.tks > dual_max_t_slices(a.b, a.n, a.r))) return hipErrorInvalidValue;
-    if (a.b <= 16) return a.n >= 16384 ? launch_decode<2, 1, 8>(a, stream) : launch_decode<1, 1, 8>(a, stream);
-    if (a.b <= 32) return a.n >= 8192 ? launch_decode<4, 2, 2>(a, stream) : launch_decode<1, 2, 4>(a, stream);
-    if (a.b <= 64) return a.n >= 8192 ? launch_decode<2, 4, 2>(a, stream) : launch_decode<1, 4, 4>(a, stream);
-    return launch_pf(a, stream);
+    int fn, fm;
+    if (!decode_shape(a.b, a.n, fn, fm)) return launch_pf(a, stream);
+    if (a.group && fn > 4) fn = 4;  // group-wise runs four waves a CTA (above): keep twice the CTAs
+    // pieces in flight per operand row (U) and waves per CTA (NW), measured per tile
+    if (fm == 1) return fn == 1 ? launch_decode<1, 1, 4, 8>(a, stream) : launch_decode<2, 1, 8, 4>(a, stream);
+    if (fm == 2) {
+        if (fn == 1) return launch_decode<1, 2, 4, 8>(a, stream);
+        if (fn == 2) return launch_decode<2, 2, 2, 8>(a, stream);
+        return fn == 4 ? launch_decode<4, 2, 1, 8>(a, stream) : launch_decode<8, 2, 1, 8>(a, stream);
+    }
+    if (fn == 1) return launch_decode<1, 4, 2, 8>(a, stream);
+    return fn == 2 ? launch_decode<2, 4, 2, 8>(a, stream) : launch_decode<4, 4, 2, 8>(a, stream);
 }
 
 int dual_max_t_slices(int64_t b, int64_t n, int r) {

@@ -39,12 +39,11 @@ __global__ __launch_bounds__(kLrThreads) void lr_scales_kernel(const uint16_t *l
     for (int64_t k = threadIdx.x; k < m; k += kLrThreads) mx = __builtin_fmaxf(mx, __builtin_fabsf(half_bits_to_float(row[k])));
     const float a1 = block_max(mx, red);
     const float s1 = a1 / kQMax;
-    uint32_t *qrow = reinterpret_cast<uint32_t *>(ql1 + (int64_t)t * (m / 2));
-    for (int64_t c8 = threadIdx.x; c8 < m / 8; c8 += kLrThreads) {
+    for (int64_t c8 = threadIdx.x; c8 < m / 8; c8 += kLrThreads) {  // Q_L1 is H's weight operand: panel layout
         int q[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) q[e] = a1 == 0.0f ? 0 : quant_code(half_bits_to_float(row[c8 * 8 + e]), s1);
-        qrow[c8] = pack8(q);
+        *reinterpret_cast<uint32_t *>(ql1 + qw_offset(t, 4 * c8, m)) = pack8(q);
     }
     mx = 0.0f;
     for (int64_t j = threadIdx.x; j < n; j += kLrThreads)

@@ -2,7 +2,8 @@
 //
 // eq. (1) of TwinQuant (page 1, section 2) applied per output channel to the
 // residual R of eq. (3): one CTA per row of W_res (fp32 [n][m]) computes
-// s_W = max|w| / 7 and writes the packed 4-bit codes in the library's format.
+// s_W = max|w| / 7 and writes the packed 4-bit codes in the library's panel layout
+// (qw_offset): a thread's 8 codes are one aligned dword of one 64-byte segment.
 #include "twq_device.h"
 #include "twq_kernels.h"
 
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_weight_kernel(const float *
     const int tid = threadIdx.x;
     const int64_t nch = m / 8;
     const float4 *wr = reinterpret_cast<const float4 *>(w + j * m);
-    uint32_t *qr = reinterpret_cast<uint32_t *>(qw + j * (m / 2));
+    auto qr = [&](int64_t c) -> uint32_t & { return *reinterpret_cast<uint32_t *>(qw + qw_offset(j, 4 * c, m)); };
     const bool cached = nch <= (int64_t)kPackThreads * kPackMaxJ;
     float4 va[kPackMaxJ], vb[kPackMaxJ];
     float mx = 0.0f;
@@ -60,11 +61,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_weight_kernel(const float *
 #pragma unroll
         for (int i = 0; i < kPackMaxJ; ++i) {
             const int64_t c = tid + (int64_t)i * kPackThreads;
-            if (c < nch) qr[c] = mx == 0.0f ? 0u : quant8_f32(va[i], vb[i], s);
+            if (c < nch) qr(c) = mx == 0.0f ? 0u : quant8_f32(va[i], vb[i], s);
         }
     } else {
         for (int64_t c = tid; c < nch; c += kPackThreads)
-            qr[c] = mx == 0.0f ? 0u : quant8_f32(wr[2 * c], wr[2 * c + 1], s);
+            qr(c) = mx == 0.0f ? 0u : quant8_f32(wr[2 * c], wr[2 * c + 1], s);
     }
 }
 
@@ -78,7 +79,6 @@ __global__ __launch_bounds__(kPackThreads) void pack_weight_grouped_kernel(const
     const int64_t j = blockIdx.x;
     const int64_t nch = m / 8;  // a multiple of 16
     const float4 *wr = reinterpret_cast<const float4 *>(w + j * m);
-    uint32_t *qr = reinterpret_cast<uint32_t *>(qw + j * (m / 2));
     for (int64_t c = threadIdx.x; c < nch; c += kPackThreads) {  // whole 16-lane groups enter together
         const float4 va = wr[2 * c], vb = wr[2 * c + 1];
         float mx = absmax8_f32(va, vb, 0.0f);
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_weight_grouped_kernel(const
         for (int off = 8; off > 0; off >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, off, kWave));
         const float s = mx / kQMax;
         if ((threadIdx.x & 15) == 0) sw[(c / 16) * n + j] = s;
-        qr[c] = mx == 0.0f ? 0u : quant8_f32(va, vb, s);
+        *reinterpret_cast<uint32_t *>(qw + qw_offset(j, 4 * c, m)) = mx == 0.0f ? 0u : quant8_f32(va, vb, s);
     }
 }
 

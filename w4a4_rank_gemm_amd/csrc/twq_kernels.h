@@ -47,6 +47,18 @@ constexpr int kGroup = 128;
 hipError_t launch_act(const ActArgs &a, const ActPlan &plan, hipStream_t stream);
 // ---- weight packer -----------------------------------------------------------------
 
+// Packed Q_W ("panel" layout; n is a multiple of 16, m of 128). Channels 16p..16p+15
+// form panel p, stored in panel order; a panel holds its m / 128 pieces (128 codes of
+// each of its 16 channels, 64 bytes a channel) one after another, and a piece holds the
+// 16 channels' 64-byte segments in channel order. So one 16-channel x 128-code MFMA
+// operand is 1 KB of contiguous memory, and a CTA that walks K reads each panel as one
+// stream. Byte q of channel j's packed codes (elements 2q and 2q + 1, low nibble first)
+// is at qw_offset(j, q, m).
+constexpr int kPanelRows = 16, kPieceBytes = 64, kPanelPiece = kPanelRows * kPieceBytes;
+__host__ __device__ constexpr int64_t qw_offset(int64_t j, int64_t q, int64_t m) {
+    return ((j / kPanelRows) * (m / 128) + q / kPieceBytes) * kPanelPiece + (j % kPanelRows) * kPieceBytes + q % kPieceBytes;
+}
+
 hipError_t launch_pack_weight(const float *w, int64_t n, int64_t m, uint8_t *qw, float *sw,
                               hipStream_t stream);
 // group-wise: s_W group-major [m / kGroup][n]
