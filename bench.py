@@ -77,7 +77,8 @@ def dual_linear_lr4_bytes(b, m, n, r):
     return b * m // 2 + 4 * b + m * n // 2 + 4 * n + b * r // 2 + 4 * b + n * r // 2 + 2 * b * n
 
 
-KERNEL_SOURCES = ("w4a4_rank_gemm_amd/csrc/dual_linear.hip", "w4a4_rank_gemm_amd/csrc/twq_device.h")
+KERNEL_SOURCES = ("w4a4_rank_gemm_amd/csrc/dual_linear.hip", "w4a4_rank_gemm_amd/csrc/twq_device.h",
+                  "w4a4_rank_gemm_amd/csrc/twq_kernels.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dual_linear_traffic.json")
 
 
