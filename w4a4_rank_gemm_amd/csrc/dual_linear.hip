@@ -359,36 +359,48 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
 // (U4); every instantiation then fits without spilling. W4A8 token rows and group-wise
 // scales take registers too, so those variants have half the pieces in flight (halved).
 constexpr int halved(int u) { return u > 4 ? u / 2 : u; }
+
+// T as a.tks partial sums: the kernel instantiated for the fewest slices (a power of two,
+// at most kMaxTSlices / RS) that hold them. Its epilogue loads every slice it is built
+// for before the main loop, so unused slices would cost (measured on the o_proj shape:
+// 16 slices for 8 used, +0.9 us).
+template <int FN, int FM, int U, int RS, int NWT, bool GRP, bool A8, int TK = 2>
+static void launch_decode_tk(const DualArgs &a, const dim3 grid, hipStream_t stream) {
+    if constexpr (2 * TK * RS <= kMaxTSlices) {
+        if (a.tks > TK) return launch_decode_tk<FN, FM, U, RS, NWT, GRP, A8, 2 * TK>(a, grid, stream);
+    }
+    hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false, TK, NWT, GRP, A8>), grid, dim3(NWT * 64), 0, stream, a);
+}
+
 template <int FN, int FM, int U, int NW, int RS>
 static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
-    constexpr int TK = RS > 0 && FN * FM <= 4 ? kMaxTSlices / RS : 1;  // partial sums of T the epilogue adds
+    constexpr bool TKS = RS > 0 && FN * FM <= 4;  // the epilogue can add T's partial sums itself
     constexpr int U4 = NW == 8 ? (2 * U < 8 ? 2 * U : 8) : U;
     constexpr bool FIT = FN * FM == 1;  // one tile: its prefetched partial sums fit eight waves
     constexpr int NWT = FIT ? NW : 4, UT = FIT ? U : U4;                      // T as partial sums
     constexpr int NWA = RS >= 8 && FN * FM >= 8 ? 4 : NW, UA = NWA == NW ? U : U4;  // W4A8, T whole
     const dim3 grid((unsigned)((a.n + FN * 16 - 1) / (FN * 16)));
-    const bool tk = TK > 1 && a.tks > 1;
+    const bool tk = TKS && a.tks > 1;
     if (a.a8) {
         if (a.acc)
             hipLaunchKernelGGL((dual_linear_decode<FN, FM, halved(U), 0, true, 1, NW, false, true>), grid, dim3(NW * 64), 0,
                                stream, a);
-        else if (tk)
-            hipLaunchKernelGGL((dual_linear_decode<FN, FM, halved(UT), RS, false, TK, NWT, false, true>), grid,
-                               dim3(NWT * 64), 0, stream, a);
-        else
+        else if (tk) {
+            if constexpr (TKS) launch_decode_tk<FN, FM, halved(UT), RS, NWT, false, true>(a, grid, stream);
+        } else
             hipLaunchKernelGGL((dual_linear_decode<FN, FM, halved(UA), RS, false, 1, NWA, false, true>), grid,
                                dim3(NWA * 64), 0, stream, a);
         return hipGetLastError();
     }
     if (a.acc)
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true, 1, NW>), grid, dim3(NW * 64), 0, stream, a);
-    else if (a.group && tk)
-        hipLaunchKernelGGL((dual_linear_decode<FN, FM, halved(U4), RS, false, TK, 4, true>), grid, dim3(256), 0, stream, a);
-    else if (a.group)
+    else if (a.group && tk) {
+        if constexpr (TKS) launch_decode_tk<FN, FM, halved(U4), RS, 4, true, false>(a, grid, stream);
+    } else if (a.group)
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, halved(U4), RS, false, 1, 4, true>), grid, dim3(256), 0, stream, a);
-    else if (tk)
-        hipLaunchKernelGGL((dual_linear_decode<FN, FM, UT, RS, false, TK, NWT>), grid, dim3(NWT * 64), 0, stream, a);
-    else
+    else if (tk) {
+        if constexpr (TKS) launch_decode_tk<FN, FM, UT, RS, NWT, false, false>(a, grid, stream);
+    } else
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false, 1, NW>), grid, dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
