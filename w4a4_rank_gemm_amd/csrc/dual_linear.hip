@@ -205,31 +205,74 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
 #pragma unroll
             for (int h = 0; h < XN; ++h) bx[fm][h] = *reinterpret_cast<const uint4 *>(xrow[fm] + c * 64 * XN + 16 * h);
     };
-    int64_t c = cb;
-    for (; c + U <= ce; c += U) {
-        uint4 bw[U][FN], bx[U][FM][XN];
-        float4 sw4[U][GRP ? FN : 1];
-        float sx1[U][GRP ? FM : 1];
+    // CTAs of 16 tiles (per-token scales, 4-bit activations) software-pipeline their
+    // batches: the loads of batch k + 1 are issued before batch k is used (pieces at or
+    // past ce reload piece ce - 1 and are not used). Measured on MI355X: 3.6-4.7% faster
+    // there; where a CTA has fewer tiles, the wasted look-ahead of the last batch costs
+    // more than the overlap gains.
+    constexpr bool PIPE = !GRP && !A8 && FN * FM >= 16;
+    if constexpr (PIPE) {
+        struct Batch {
+            uint4 bw[U][FN], bx[U][FM][XN];
+        };
+        const float4 no_sw[1] = {};
+        const float no_sx[1] = {};
+        auto load_batch = [&](int64_t c0, Batch &bt) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < U; ++u) {
+                const int64_t cu = c0 + u < ce ? c0 + u : ce - 1;
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) bw[u][fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (c - cb + u) * kPanelPiece);
-            load_x(c + u, bx[u]);
-            load_scales(c + u, sw4[u], sx1[u]);
+                for (int fn = 0; fn < FN; ++fn)
+                    bt.bw[u][fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (cu - cb) * kPanelPiece);
+                load_x(cu, bt.bx[u]);
+            }
+        };
+        auto use_batch = [&](int64_t c0, Batch &bt) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (c0 + u < ce) mma(bt.bw[u], bt.bx[u], no_sw, no_sx);
+        };
+        if (cb < ce) {
+            Batch ba, bb;
+            load_batch(cb, ba);
+            for (int64_t c = cb;; c += 2 * U) {
+                load_batch(c + U, bb);
+                __builtin_amdgcn_sched_barrier(0);  // the next batch in flight before this one is used
+                use_batch(c, ba);
+                if (c + U >= ce) break;
+                load_batch(c + 2 * U, ba);
+                __builtin_amdgcn_sched_barrier(0);
+                use_batch(c + U, bb);
+                if (c + 2 * U >= ce) break;
+            }
         }
-        __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of its first use
+    } else {
+        int64_t c = cb;
+        for (; c + U <= ce; c += U) {
+            uint4 bw[U][FN], bx[U][FM][XN];
+            float4 sw4[U][GRP ? FN : 1];
+            float sx1[U][GRP ? FM : 1];
 #pragma unroll
-        for (int u = 0; u < U; ++u) mma(bw[u], bx[u], sw4[u], sx1[u]);
-    }
-    for (; c < ce; ++c) {
-        uint4 bw[FN], bx[FM][XN];
-        float4 sw4[GRP ? FN : 1];
-        float sx1[GRP ? FM : 1];
+            for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) bw[fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (c - cb) * kPanelPiece);
-        load_x(c, bx);
-        load_scales(c, sw4, sx1);
-        mma(bw, bx, sw4, sx1);
+                for (int fn = 0; fn < FN; ++fn) bw[u][fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (c - cb + u) * kPanelPiece);
+                load_x(c + u, bx[u]);
+                load_scales(c + u, sw4[u], sx1[u]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of its first use
+#pragma unroll
+            for (int u = 0; u < U; ++u) mma(bw[u], bx[u], sw4[u], sx1[u]);
+        }
+        for (; c < ce; ++c) {
+            uint4 bw[FN], bx[FM][XN];
+            float4 sw4[GRP ? FN : 1];
+            float sx1[GRP ? FM : 1];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) bw[fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (c - cb) * kPanelPiece);
+            load_x(c, bx);
+            load_scales(c, sw4, sx1);
+            mma(bw, bx, sw4, sx1);
+        }
     }
 
     // Without the prefetch above (a wave owns several epilogue tiles), the low-rank
@@ -821,7 +864,7 @@ hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream) {
         return fn == 4 ? launch_decode<4, 2, 1, 8>(a, stream) : launch_decode<8, 2, 1, 8>(a, stream);
     }
     if (fn == 1) return launch_decode<1, 4, 2, 8>(a, stream);
-    return fn == 2 ? launch_decode<2, 4, 2, 8>(a, stream) : launch_decode<4, 4, 2, 8>(a, stream);
+    return fn == 2 ? launch_decode<2, 4, 2, 8>(a, stream) : launch_decode<4, 4, 1, 8>(a, stream);
 }
 
 int dual_max_t_slices(int64_t b, int64_t n, int r) {
