@@ -130,9 +130,10 @@ RAGGED = [
     (129, 1152, 208, 64), (16, 256, 256, 240),
     # few-token launch shapes whose CTAs own more output tiles than waves
     (32, 1024, 8192, 64), (64, 512, 8192, 32), (16, 512, 16384, 16), (27, 512, 8208, 48),
-    # 16-tile CTAs (8x2 and 4x4 blocks of 16), whose main loop is software-pipelined: 3 and
-    # 2 K pieces for 8 waves (most waves get none), a partial last channel tile
-    (27, 384, 24592, 32), (64, 256, 12304, 48),
+    # wide few-token grids with a partial last channel tile; 16-tile CTAs (8x2 and 4x4
+    # blocks of 16), whose main loop is software-pipelined: 64 K pieces for 8 waves, and
+    # 2 pieces for 8 waves (most waves get none)
+    (27, 384, 24592, 32), (27, 8192, 24592, 16), (64, 256, 12304, 48),
 ]
 
 

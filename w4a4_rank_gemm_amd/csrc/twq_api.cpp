@@ -47,7 +47,7 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 LinearLayout linear_layout(int64_t b, int64_t m, int64_t n, int64_t r, int group, int a8 = 0) {
     LinearLayout L{};
     L.plan = twq::plan_act(b, m, r);
-    L.direct = r > 0 && L.plan.mode == 1 && L.plan.ks > 1 && L.plan.ks <= twq::dual_max_t_slices(b, n, (int)r);
+    L.direct = r > 0 && L.plan.mode == 1 && L.plan.ks > 1 && L.plan.ks <= twq::dual_max_t_slices(b, m, n, (int)r);
     L.qx = 0;
     L.sx = align256((size_t)(a8 ? b * m : b * m / 2));
     L.t = L.sx + align256((size_t)b * 4 * (size_t)(group ? m / group : 1));

@@ -93,7 +93,7 @@ hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream);
 
 // Largest number of T partial-sum slices the dual launch for this shape adds itself
 // (1: it needs T whole).
-int dual_max_t_slices(int64_t b, int64_t n, int r);
+int dual_max_t_slices(int64_t b, int64_t m, int64_t n, int r);
 
 // ---- int4 low-rank variant ------------------------------------------------------------
 
