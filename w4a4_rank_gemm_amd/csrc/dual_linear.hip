@@ -205,18 +205,19 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
 #pragma unroll
             for (int h = 0; h < XN; ++h) bx[fm][h] = *reinterpret_cast<const uint4 *>(xrow[fm] + c * 64 * XN + 16 * h);
     };
-    // CTAs of 16 tiles (per-token scales, 4-bit activations) software-pipeline their
-    // batches: the loads of batch k + 1 are issued before batch k is used (pieces at or
-    // past ce reload piece ce - 1 and are not used). Measured on MI355X: 3.6-4.7% faster
-    // there; where a CTA has fewer tiles, the wasted look-ahead of the last batch costs
-    // more than the overlap gains.
-    constexpr bool PIPE = !GRP && !A8 && FN * FM >= 16;
+    // Software-pipelined batches: the loads of batch k + 1 are issued before batch k is
+    // used (pieces at or past ce reload piece ce - 1 and are not used). Measured on
+    // MI355X: per-token W4A4 CTAs of 16 tiles 3.6-4.7% faster, with fewer tiles the wasted
+    // look-ahead of the last batch costs more than the overlap gains; the group-wise
+    // variant, whose pieces each carry their scales and an fp32 update, 6-67% faster on
+    // every tiling but 2 x 1 blocks (3% slower there); W4A8 2-8% slower.
+    constexpr bool PIPE = (!GRP && !A8 && FN * FM >= 16) || (GRP && !(FN == 2 && FM == 1));
     if constexpr (PIPE) {
         struct Batch {
             uint4 bw[U][FN], bx[U][FM][XN];
+            float4 sw4[U][GRP ? FN : 1];
+            float sx1[U][GRP ? FM : 1];
         };
-        const float4 no_sw[1] = {};
-        const float no_sx[1] = {};
         auto load_batch = [&](int64_t c0, Batch &bt) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -225,12 +226,13 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
                 for (int fn = 0; fn < FN; ++fn)
                     bt.bw[u][fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (cu - cb) * kPanelPiece);
                 load_x(cu, bt.bx[u]);
+                load_scales(cu, bt.sw4[u], bt.sx1[u]);
             }
         };
         auto use_batch = [&](int64_t c0, Batch &bt) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (c0 + u < ce) mma(bt.bw[u], bt.bx[u], no_sw, no_sx);
+                if (c0 + u < ce) mma(bt.bw[u], bt.bx[u], bt.sw4[u], bt.sx1[u]);
         };
         if (cb < ce) {
             Batch ba, bb;
@@ -399,8 +401,8 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
 // A 512-thread CTA gives a wave at most 256 registers. The variants that hold more --
 // T's partial sums prefetched for a CTA of several tiles, the group-wise fp32 sums --
 // run four waves instead, each over twice the K range with twice the pieces in flight
-// (U4); every instantiation then fits without spilling. W4A8 token rows and group-wise
-// scales take registers too, so those variants have half the pieces in flight (halved).
+// (U4); every instantiation then fits without spilling. W4A8 token rows take registers
+// too, so that variant has half the pieces in flight (halved).
 constexpr int halved(int u) { return u > 4 ? u / 2 : u; }
 
 // T as a.tks partial sums: the kernel instantiated for the fewest slices (a power of two,
@@ -422,6 +424,8 @@ static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
     constexpr bool FIT = FN * FM == 1;  // one tile: its prefetched partial sums fit eight waves
     constexpr int NWT = FIT ? NW : 4, UT = FIT ? U : U4;                      // T as partial sums
     constexpr int NWA = RS >= 8 && FN * FM >= 8 ? 4 : NW, UA = NWA == NW ? U : U4;  // W4A8, T whole
+    // group-wise (four waves, pipelined but for 2 x 1 blocks): pieces per batch measured per tiling
+    constexpr int UG = FN * FM == 1 || (FN == 2 && FM == 1) ? 4 : FM == 2 && FN <= 2 ? 2 : 1;
     const dim3 grid((unsigned)((a.n + FN * 16 - 1) / (FN * 16)));
     const bool tk = TKS && a.tks > 1;
     if (a.a8) {
@@ -438,9 +442,9 @@ static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
     if (a.acc)
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true, 1, NW>), grid, dim3(NW * 64), 0, stream, a);
     else if (a.group && tk) {
-        if constexpr (TKS) launch_decode_tk<FN, FM, halved(U4), RS, 4, true, false>(a, grid, stream);
+        if constexpr (TKS) launch_decode_tk<FN, FM, UG, RS, 4, true, false>(a, grid, stream);
     } else if (a.group)
-        hipLaunchKernelGGL((dual_linear_decode<FN, FM, halved(U4), RS, false, 1, 4, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, 1, 4, true>), grid, dim3(256), 0, stream, a);
     else if (tk) {
         if constexpr (TKS) launch_decode_tk<FN, FM, UT, RS, NWT, false, false>(a, grid, stream);
     } else
