@@ -52,13 +52,14 @@ __device__ __forceinline__ v4i lr4_tile(const DualArgs &a, int64_t ch_row, int64
 // ---------------------------------------------------------------------------------
 // Few tokens (b <= 64): the layer streams Q_W once from HBM and little else. A CTA
 // owns FN*16 output channels and all tokens (FM tiles of 16); its NW waves split
-// K and feed the matrix cores straight from global memory, U 16-byte loads per
-// operand row issued before any is consumed (a weight operand is one contiguous 1 KB
-// piece of a panel, so each wave streams FN contiguous runs); the NW partial accumulators are
-// added through LDS. Loads are unconditional -- rows past n or b are clamped to a
-// valid row and their outputs never stored -- so nothing serialises them, and the
-// low-rank operands of the epilogue are loaded first so their latency hides under
-// the main loop.
+// K and feed the matrix cores straight from global memory in batches of U 16-byte
+// loads per operand row, every load of a batch issued before any is consumed (a
+// weight operand is one contiguous 1 KB piece of a panel, so each wave streams FN
+// contiguous runs; some variants also issue the next batch before using the current
+// one, see PIPE); the NW partial accumulators are added through LDS. Loads are
+// unconditional -- rows past n or b are clamped to a valid row and their outputs never
+// stored -- so nothing serialises them, and the low-rank operands of the epilogue are
+// loaded first so their latency hides under the main loop.
 // Most partial sums of T (K slices x 32-rank steps) one lane of a decode epilogue
 // holds; a shape with more slices gets T reduced first.
 constexpr int kMaxTSlices = 16;
@@ -400,9 +401,10 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
 
 // A 512-thread CTA gives a wave at most 256 registers. The variants that hold more --
 // T's partial sums prefetched for a CTA of several tiles, the group-wise fp32 sums --
-// run four waves instead, each over twice the K range with twice the pieces in flight
-// (U4); every instantiation then fits without spilling. W4A8 token rows take registers
-// too, so that variant has half the pieces in flight (halved).
+// run four waves instead, each over twice the K range: the first with twice the pieces
+// in flight (U4), the group-wise one with its own measured count per tiling (UG); every
+// instantiation then fits without spilling. W4A8 token rows take registers too, so
+// that variant has half the pieces in flight (halved).
 constexpr int halved(int u) { return u > 4 ? u / 2 : u; }
 
 // T as a.tks partial sums: the kernel instantiated for the fewest slices (a power of two,
