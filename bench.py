@@ -111,6 +111,23 @@ def lowrank_storage_ratio(m, n, r):
     return 2 * r * (m + n) / (m * n / 2)
 
 
+# The oracle's work per call is linear in the tokens (rows are independent), so shapes
+# whose whole call would take the host much longer than the budget are timed on their
+# first rows and scaled to the batch: at most this many multiply-adds of the residual
+# product per timed call (about 7 s on 16 host threads).
+CPU_MACS_PER_CALL = 3e11
+
+
+def _cpu_rows(b, m, n):
+    return int(min(b, max(16, CPU_MACS_PER_CALL // (m * n))))
+
+
+def _cpu_sample(calls, rows, b, m, n, r, el, what):
+    part = "whole calls" if rows == b else f"calls on the first {rows} of {b} tokens, scaled to the whole batch,"
+    return (f"{calls} {what}{part} of the same workload (b={b}, m={m}, n={n}, r={r}) in {el:.1f} s; "
+            "weights quantized once outside the timing")
+
+
 def _cpu_baseline_grouped(d, g, budget_s=12.0):
     """The group-wise oracle on the host, weights pre-quantized, on the first rows of the
     batch (the per-group integer sums of every row would not fit in memory at full size);
@@ -153,23 +170,24 @@ def _cpu_baseline_a8(d, budget_s=12.0):
     b, m = x.shape
     n, r = w.shape[0], l1t.shape[0]
     qw, _, sw = oracle.quantize_weight(w)  # offline packing, not timed
+    rows = _cpu_rows(b, m, n)
+    xs = np.ascontiguousarray(x[:rows])
     calls = 0
     t0 = time.perf_counter()
     while True:
-        qx, sx = oracle.quantize_act_a8(x)
+        qx, sx = oracle.quantize_act_a8(xs)
         acc = oracle.residual_acc(qx, qw)
         y = sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] * acc
         if r:
-            y += oracle.lowrank_out(oracle.lowrank_t(x, l1t), l2t)
+            y += oracle.lowrank_out(oracle.lowrank_t(xs, l1t), l2t)
         calls += 1
         el = time.perf_counter() - t0
         if el >= budget_s or calls >= 1000:
             break
-    sec = el / calls
+    sec = el / calls * b / rows
     return {"value": layer_ops(b, m, n, r) / sec / 1e12, "unit": "TOPS", "cores": oracle.max_threads(),
             "kind": "oracle", "ms_per_call": sec * 1e3,
-            "sample": f"{calls} whole W4A8 calls of the same workload (b={b}, m={m}, n={n}, r={r}) "
-                      f"in {el:.1f} s; weights quantized once outside the timing"}
+            "sample": _cpu_sample(calls, rows, b, m, n, r, el, "W4A8 ")}
 
 
 def _cpu_baseline(d, budget_s=12.0, lr4=False):
@@ -182,6 +200,8 @@ def _cpu_baseline(d, budget_s=12.0, lr4=False):
     n, r = w.shape[0], l1t.shape[0]
     qw, _, sw = oracle.quantize_weight(w)  # offline packing, not timed
     lq = oracle.quantize_lowrank(l1t, l2t) if (lr4 and r) else None
+    rows = _cpu_rows(b, m, n)
+    x = np.ascontiguousarray(x[:rows])
     calls = 0
     t0 = time.perf_counter()
     while True:
@@ -197,11 +217,10 @@ def _cpu_baseline(d, budget_s=12.0, lr4=False):
         el = time.perf_counter() - t0
         if el >= budget_s or calls >= 1000:
             break
-    sec = el / calls
+    sec = el / calls * b / rows
     return {"value": layer_ops(b, m, n, r) / sec / 1e12, "unit": "TOPS", "cores": oracle.max_threads(),
             "kind": "oracle", "ms_per_call": sec * 1e3,
-            "sample": f"{calls} whole calls of the same workload (b={b}, m={m}, n={n}, r={r}) "
-                      f"in {el:.1f} s; weights quantized once outside the timing"}
+            "sample": _cpu_sample(calls, rows, b, m, n, r, el, "")}
 
 
 def _graph_time(fn, steps, warmup, stream):
