@@ -128,6 +128,9 @@ RAGGED = [
     (1, 128, 16, 16), (17, 384, 48, 32), (33, 512, 80, 48), (130, 640, 144, 16),
     (5, 256, 272, 0), (64, 1024, 128, 128), (200, 256, 272, 256), (2, 4096, 32, 32),
     (129, 1152, 208, 64), (16, 256, 256, 240),
+    # the many-token kernel from b = 65, while the activation launch keeps its few-token
+    # form up to b = 128
+    (65, 384, 176, 32), (128, 512, 144, 48),
     # few-token launch shapes whose CTAs own more output tiles than waves
     (32, 1024, 8192, 64), (64, 512, 8192, 32), (16, 512, 16384, 16), (27, 512, 8208, 48),
     # wide few-token grids with a partial last channel tile; 16-tile CTAs (8x2 and 4x4
