@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 matrix cores, TOP/s
 ROTATE_BYTES = 512 << 20     # working set that defeats L2 + Infinity Cache reuse
-BASELINE_METRIC = "fused W4A4+low-rank linear: \u00b5s/call, effective TOPS, % int8-MFMA/HBM roofline"
+METRIC_NAME = "fused W4A4+low-rank linear: \u00b5s/call, effective TOPS, % int8-MFMA/HBM roofline"
 
 
 def layer_ops(b, m, n, r):
@@ -573,7 +573,7 @@ def main():
     else:
         entry_points = f"twq_quantize_act{sfx}+twq_dual_linear{sfx}"
     out = {
-        "metric": BASELINE_METRIC,
+        "metric": METRIC_NAME,
         "value": round(tops, 3),
         "unit": "TOPS",
         "n_gpus": 1,

@@ -59,7 +59,7 @@ def lib() -> ctypes.CDLL:
             if _lib is None:
                 if not os.path.exists(LIB_PATH):
                     raise ImportError(f"libtwq.so is not built ({LIB_PATH}); run "
-                                      "`python -c 'import __graft_entry__ as g; g.build()'`")
+                                      "`python -m w4a4_rank_gemm_amd.build`")
                 L = ctypes.CDLL(LIB_PATH)
                 L.twq_status_string.restype = ctypes.c_char_p
                 L.twq_status_string.argtypes = [ctypes.c_int]
