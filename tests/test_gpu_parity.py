@@ -147,6 +147,27 @@ def test_ragged_shapes(b, m, n, r):
     check_full(d, run_gpu(d))
 
 
+def _random_shapes(count, seed=2026, max_macs=6e8):
+    """Seeded shapes across the launch rules: b in each token range of the few-token
+    tilings and beyond, m and n anywhere on their grids, r any multiple of 16 up to 128."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        lo, hi = [(1, 17), (17, 33), (33, 65), (65, 300)][int(rng.integers(0, 4))]
+        b, m = int(rng.integers(lo, hi)), 128 * int(rng.integers(1, 40))
+        n, r = 16 * int(rng.integers(1, 1600)), 16 * int(rng.integers(0, 9))
+        if b * m * n <= max_macs:
+            out.append((b, m, n, r))
+    return out
+
+
+@pytest.mark.parametrize("b,m,n,r", _random_shapes(12))
+def test_seeded_random_shapes(b, m, n, r):
+    _say(f"random shape b={b} m={m} n={n} r={r}")
+    d = synth.make_random(b, m, n, r, seed=b + m + n + r)
+    check_full(d, run_gpu(d))
+
+
 def test_zero_rows_and_zero_residual():
     """An all-zero token row (s_X = 0) and W_res = 0 (pure low-rank, s_W = 0)."""
     d = synth.make_random(24, 512, 96, 32, seed=11)
