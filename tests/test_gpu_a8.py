@@ -14,6 +14,7 @@ import torch
 import oracle
 import synth
 import w4a4_rank_gemm_amd as twq
+from tests.test_gpu_parity import _random_shapes
 from tests.panels import to_panels
 
 pytestmark = pytest.mark.gpu
@@ -64,7 +65,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("b,m,n,r", SHAPES)
+@pytest.mark.parametrize("b,m,n,r", SHAPES + _random_shapes(8, seed=2028))
 def test_a8_matches_oracle(b, m, n, r):
     _say(f"a8 b={b} m={m} n={n} r={r}")
     d = synth.make_random(b, m, n, r, seed=700 + b + n)

@@ -14,6 +14,7 @@ import torch
 import oracle
 import synth
 import w4a4_rank_gemm_amd as twq
+from tests.test_gpu_parity import _random_shapes
 from tests.panels import to_panels
 from tests.test_gpu_quant_ties import _row
 
@@ -77,7 +78,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("b,m,n,r", SHAPES)
+@pytest.mark.parametrize("b,m,n,r", SHAPES + _random_shapes(8, seed=2027))
 def test_grouped_matches_oracle(b, m, n, r):
     _say(f"grouped b={b} m={m} n={n} r={r}")
     d = synth.make_random(b, m, n, r, seed=500 + b + n)
