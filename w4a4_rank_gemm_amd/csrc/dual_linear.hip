@@ -225,7 +225,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
                 const int64_t cu = c0 + u < ce ? c0 + u : ce - 1;
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
-                    bt.bw[u][fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (cu - cb) * kPanelPiece);
+                    bt.bw[u][fn] = load_stream16(wrow[fn] + (cu - cb) * kPanelPiece);
                 load_x(cu, bt.bx[u]);
                 load_scales(cu, bt.sw4[u], bt.sx1[u]);
             }
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn) bw[u][fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (c - cb + u) * kPanelPiece);
+                for (int fn = 0; fn < FN; ++fn) bw[u][fn] = load_stream16(wrow[fn] + (c - cb + u) * kPanelPiece);
                 load_x(c + u, bx[u]);
                 load_scales(c + u, sw4[u], sx1[u]);
             }
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
             float4 sw4[GRP ? FN : 1];
             float sx1[GRP ? FM : 1];
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) bw[fn] = *reinterpret_cast<const uint4 *>(wrow[fn] + (c - cb) * kPanelPiece);
+            for (int fn = 0; fn < FN; ++fn) bw[fn] = load_stream16(wrow[fn] + (c - cb) * kPanelPiece);
             load_x(c, bx);
             load_scales(c, sw4, sx1);
             mma(bw, bx, sw4, sx1);

