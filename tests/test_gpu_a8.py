@@ -61,7 +61,7 @@ SHAPES = [
     (130, 640, 144, 16), (200, 256, 272, 256), (129, 1152, 208, 64), (32, 1024, 8192, 64),
     (16, 512, 16384, 16), (5, 2048, 16384, 64), (300, 4096, 1040, 32), (27, 512, 8208, 48),
     # wide few-token grids: 2x2 and 4x4 blocks of 16 per CTA, a partial last channel tile
-    (27, 384, 24592, 32), (64, 256, 12304, 48),
+    (27, 384, 24592, 32), (64, 256, 12304, 48), (48, 512, 8192, 32),
 ]
 
 
