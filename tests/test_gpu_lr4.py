@@ -88,7 +88,9 @@ def test_lr4_hand_worked_padded():
 
 
 SHAPES = [(16, 512, 512, 32), (17, 384, 80, 64), (1, 256, 256, 256), (130, 640, 144, 96),
-          (32, 1024, 8192, 128), (64, 512, 8192, 32), (200, 256, 176, 160)]
+          (32, 1024, 8192, 128), (64, 512, 8192, 32), (200, 256, 176, 160),
+          # the remaining few-token tilings (2x1 blocks; 4x4, pipelined) and b just above 64
+          (16, 512, 8192, 32), (64, 256, 12304, 64), (90, 384, 272, 32)]
 
 
 @pytest.mark.parametrize("b,m,n,r", SHAPES)
