@@ -608,11 +608,13 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 // times s_X s_W.
 //
 // W4A8 (A8): a token row holds one int8 code per element, 128 bytes per stage, stored as
-// two 64-byte half rows (the first BM rows of the token part hold bytes 0-63 of each
-// token's slice, the next BM rows bytes 64-127), so the layout and the loads above apply
-// unchanged. Lane (li, g) needs codes 32g..32g+31 of its token: chunks 2 (g % 2) and
-// 2 (g % 2) + 1 of half row g / 2, permuted into the expanded weight operand's lane order
-// (perm16); the accumulator holds 16 acc.
+// two 64-byte rows e = 0, 1 (the first BM rows of the token part and the next BM): row e
+// holds bytes 32c + 16e .. 32c + 16e + 15 of the token's slice at chunk position c, so the
+// layout, the loads and the lane -> address map of the reads above apply unchanged. Lane
+// (li, g) needs codes 32g..32g+31 of its token: chunk g of rows 0 and 1, read exactly
+// like the 4-bit token operand (splitting the slice into bytes 0-63 and 64-127 instead
+// gave lanes g and g + 2 the same banks: LDS bank conflicts, 2-3.6% slower), permuted
+// into the expanded weight operand's lane order (perm16); the accumulator holds 16 acc.
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false,
           bool A8 = false>
 __global__ __launch_bounds__(WN * WM * 64, A8 ? (S > 2 ? 2 : 3) : (S == 2 ? 4 : 3))
@@ -672,8 +674,9 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
             const int64_t tok = tok0 + (row - BN) % BM;
             rel = (tok < a.b ? tok : a.b - 1) - tok0;
         }
-        // A8: token rows BN + h BM + t hold bytes 64 h .. 64 h + 63 of token t's slice
-        off[j] = (uint32_t)(row < BN ? qw_offset(rel, chunk * 16, a.m) : rel * xb + ((row - BN) / BM) * 64 + chunk * 16);
+        // A8: chunk c of token row BN + e BM + t holds bytes 32 c + 16 e .. + 15 of token t's slice
+        off[j] = (uint32_t)(row < BN ? qw_offset(rel, chunk * 16, a.m)
+                                     : rel * xb + (A8 ? chunk * 32 + ((row - BN) / BM) * 16 : chunk * 16));
     }
     __shared__ __attribute__((aligned(16))) uint8_t ring[S * SLOT];
     // GRP: this thread's scale: waves 0-1 load s_W of channel ch0 + tid, waves 2-3 s_X of
@@ -734,14 +737,13 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
         rda[h] = lds_offset(ring) + lane_off + (wn * (BN / WN) / 16) * BLK;
         rdb[h] = lds_offset(ring) + lane_off + ((BN + wm * (BM / WM)) / 16) * BLK;
     }
-    // A8: this lane's two chunks of its half row (64-byte rows: line li / 2, position
-    // (4 (li % 2) + c) ^ (li / 2))
+    // A8: this lane's chunk g of token rows e = 0, 1 (as the 4-bit token operand: line
+    // li / 2, position (4 (li % 2) + g) ^ (li / 2))
     uint32_t rdx[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        const int c = 2 * (g % 2) + e;
-        rdx[e] = lds_offset(ring) + (li / 2) * 128 + ((4 * (li % 2) + c) ^ (li / 2)) * 16 +
-                 ((BN + (g / 2) * BM + wm * (BM / WM)) / 16) * BLK;
+        rdx[e] = lds_offset(ring) + (li / 2) * 128 + ((4 * (li % 2) + g) ^ (li / 2)) * 16 +
+                 ((BN + e * BM + wm * (BM / WM)) / 16) * BLK;
     }
 
     // Step st issues stage st into slot st % S and consumes stage st - (S - 1). Every
