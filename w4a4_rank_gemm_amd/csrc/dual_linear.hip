@@ -49,6 +49,14 @@ __device__ __forceinline__ v4i lr4_tile(const DualArgs &a, int64_t ch_row, int64
     return acc2;
 }
 
+// Block b runs on XCD b % 8 (the hardware deals CTAs out in turn). Give XCD x the
+// contiguous range of q + (x < rem) tiles starting at x q + min(x, rem), q = tiles / 8,
+// rem = tiles % 8: a bijection of [0, tiles) for any tile count.
+__host__ __device__ __forceinline__ int64_t xcd_order(int64_t bid, int64_t ntiles) {
+    const int64_t q = ntiles / 8, rem = ntiles % 8, x = bid % 8, j = bid / 8;
+    return x * q + (x < rem ? x : rem) + j;
+}
+
 // ---------------------------------------------------------------------------------
 // Few tokens (b <= 64): the layer streams Q_W once from HBM and little else. A CTA
 // owns FN*16 output channels and all tokens (FM tiles of 16); its NW waves split
@@ -82,7 +90,9 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
     __shared__ v4i red[NW][FN * FM][kWave];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int li = lane & 15, g = lane >> 4;
-    const int64_t ch0 = (int64_t)blockIdx.x * (FN * 16);
+    // GRP: neighbouring channel tiles on one XCD, so the two halves of a 128-byte line of
+    // s_W (one group row, FN = 4: 64 bytes a tile) are fetched into the same L2 once
+    const int64_t ch0 = (GRP ? xcd_order(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x) * (FN * 16);
     const int64_t kb = a.m / 2;
     const int64_t nch = a.m / 128;  // 64-byte pieces of a packed row
     const int64_t cb = wave * nch / NW, ce = (wave + 1) * nch / NW;
@@ -486,14 +496,6 @@ static hipError_t launch_decode(const DualArgs &a, hipStream_t stream) {
 // to the eight XCDs in turn): each XCD walks a contiguous range of tiles ordered in
 // groups of GM token tiles, so the CTAs an XCD runs at once share W and Q_X tiles in
 // that XCD's L2.
-
-// Block b runs on XCD b % 8 (the hardware deals CTAs out in turn). Give XCD x the
-// contiguous range of q + (x < rem) tiles starting at x q + min(x, rem), q = tiles / 8,
-// rem = tiles % 8: a bijection of [0, tiles) for any tile count.
-__host__ __device__ __forceinline__ int64_t xcd_order(int64_t bid, int64_t ntiles) {
-    const int64_t q = ntiles / 8, rem = ntiles % 8, x = bid % 8, j = bid / 8;
-    return x * q + (x < rem ? x : rem) + j;
-}
 
 // Second half of the many-token epilogue, from the dequantized residual y of a wave's
 // FN x FM tiles of 16 x 16 (the wave at (wn, wm) of a BN x BM CTA tile at (ch0, tok0)):
