@@ -137,6 +137,9 @@ RAGGED = [
     # blocks of 16), whose main loop is software-pipelined: 64 K pieces for 8 waves, and
     # 2 pieces for 8 waves (most waves get none)
     (27, 384, 24592, 32), (27, 8192, 24592, 16), (64, 256, 12304, 48),
+    # 4x4-block CTAs whose waves read their K slices of Q_X from LDS (a full slice of
+    # four pieces a wave; a ragged token count and a partial last channel tile)
+    (64, 4096, 14336, 64), (49, 2048, 12304, 32),
 ]
 
 

@@ -81,7 +81,8 @@ constexpr int kMaxTSlices = 16;
 // weight row pairs with 128 bytes of each token row; those are permuted into the lane
 // order of the expanded weight operand (perm16) and used unscaled, so the accumulator
 // holds 16 acc.
-template <int FN, int FM, int U, int RS, bool STORE_ACC, int TK = 1, int NW = 4, bool GRP = false, bool A8 = false>
+template <int FN, int FM, int U, int RS, bool STORE_ACC, int TK = 1, int NW = 4, bool GRP = false, bool A8 = false,
+          bool XL = false>
 __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
     static_assert(!(GRP && STORE_ACC), "group-wise sums are stored dequantized only");
     static_assert(!(GRP && A8), "group-wise scales with 4-bit activations only");
@@ -111,6 +112,16 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
         const int64_t tok = fm * 16 + li;
         xrow[fm] = a.qx + (tok < a.b ? tok : a.b - 1) * (A8 ? a.m : kb) + g * 16 * XN;
     }
+    // XL (per-token 4 x 4 tiles, K short enough): each wave copies its K slice of Q_X (its
+    // pieces x FM token tiles, 1 KB a block) into its own part of the LDS that the
+    // cross-wave reduction fills afterwards, by direct-to-LDS loads issued ahead of the
+    // weight stream; the main loop then reads X from LDS and only the weights stream from
+    // memory. Lane l of the copy of block (piece c, tile fm) fetches bytes 64 c + 16 (l % 4)
+    // of token row 16 fm + l / 4, so a block holds 64-byte rows in token order, read back
+    // by lane (li, g) at 64 li + 16 g. The launcher picks XL only where a wave's slice fits
+    // its part of red: at most FN pieces a wave, ceil(m / 128 / NW) <= FN.
+    static_assert(!XL || (!GRP && !A8 && FN * FM >= 16), "X slices in LDS: pipelined per-token tiles");
+    uint8_t *const xls = reinterpret_cast<uint8_t *>(&red[wave][0][0]);
 
     // Epilogue tiles are dealt to the waves in turn (tile t to wave t % NW). When a
     // wave owns one tile, its low-rank operands are loaded here, ahead of the main
@@ -211,10 +222,28 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
         }
     };
     auto load_x = [&](int64_t c, uint4 (&bx)[FM][XN]) {
+        if constexpr (XL) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                bx[fm][0] = *reinterpret_cast<const uint4 *>(xls + ((c - cb) * FM + fm) * 1024 + li * 64 + g * 16);
+            return;
+        }
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int h = 0; h < XN; ++h) bx[fm][h] = *reinterpret_cast<const uint4 *>(xrow[fm] + c * 64 * XN + 16 * h);
+    };
+    auto copy_x = [&]() {  // this wave's slice of Q_X into LDS (XL)
+        const __amdgpu_buffer_rsrc_t rq =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.qx), 0, 0x7fffffff, 0x00020000);
+        for (int64_t c = cb; c < ce; ++c)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int64_t tok = fm * 16 + lane / 4;
+                const int64_t off = (tok < a.b ? tok : a.b - 1) * kb + c * 64 + (lane % 4) * 16;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rq, (__attribute__((address_space(3))) void *)(xls + ((c - cb) * FM + fm) * 1024), 16, (int)off, 0, 0, 0);
+            }
     };
     // Software-pipelined batches: the loads of batch k + 1 are issued before batch k is
     // used (pieces at or past ce reload piece ce - 1 and are not used). Measured on
@@ -229,14 +258,14 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
             float4 sw4[U][GRP ? FN : 1];
             float sx1[U][GRP ? FM : 1];
         };
-        auto load_batch = [&](int64_t c0, Batch &bt) {
+        auto load_batch = [&](int64_t c0, Batch &bt, bool with_x = true) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t cu = c0 + u < ce ? c0 + u : ce - 1;
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
                     bt.bw[u][fn] = load_stream16(wrow[fn] + (cu - cb) * kPanelPiece);
-                load_x(cu, bt.bx[u]);
+                if (with_x) load_x(cu, bt.bx[u]);
                 load_scales(cu, bt.sw4[u], bt.sx1[u]);
             }
         };
@@ -247,7 +276,18 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
         };
         if (cb < ce) {
             Batch ba, bb;
-            load_batch(cb, ba);
+            if constexpr (XL) {
+                // the copy of X first, then the first batch's weights; once at most those
+                // weight loads are outstanding the copy has landed and X is read from LDS
+                copy_x();
+                load_batch(cb, ba, false);
+                wait_vmcnt<U * FN>();
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int u = 0; u < U; ++u) load_x(cb + u < ce ? cb + u : ce - 1, ba.bx[u]);
+            } else {
+                load_batch(cb, ba);
+            }
             for (int64_t c = cb;; c += 2 * U) {
                 load_batch(c + U, bb);
                 __builtin_amdgcn_sched_barrier(0);  // the next batch in flight before this one is used
@@ -451,15 +491,27 @@ static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
                                dim3(NWA * 64), 0, stream, a);
         return hipGetLastError();
     }
-    if (a.acc)
-        hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true, 1, NW>), grid, dim3(NW * 64), 0, stream, a);
-    else if (a.group && tk) {
+    // per-token 4 x 4 tiles with every wave's K slice of Q_X within its part of the LDS
+    // reduction buffer: X read from LDS (measured on MI355X: +8-11% at 49-64 tokens,
+    // m = 4096; no gain on 8 x 2 tiles)
+    constexpr bool XLT = FN == 4 && FM == 4;
+    const bool xl = XLT && (a.m / 128 + NW - 1) / NW <= FN;
+    if (a.acc) {
+        if (xl)
+            hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true, 1, NW, false, false, XLT>), grid, dim3(NW * 64), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true, 1, NW>), grid, dim3(NW * 64), 0, stream, a);
+    } else if (a.group && tk) {
         if constexpr (TKS) launch_decode_tk<FN, FM, UG, RS, 4, true, false>(a, grid, stream);
     } else if (a.group)
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, 1, 4, true>), grid, dim3(256), 0, stream, a);
     else if (tk) {
         if constexpr (TKS) launch_decode_tk<FN, FM, UT, RS, NWT, false, false>(a, grid, stream);
-    } else
+    } else if (xl)
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false, 1, NW, false, false, XLT>), grid, dim3(NW * 64), 0,
+                           stream, a);
+    else
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false, 1, NW>), grid, dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
