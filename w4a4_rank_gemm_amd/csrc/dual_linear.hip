@@ -112,7 +112,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
         const int64_t tok = fm * 16 + li;
         xrow[fm] = a.qx + (tok < a.b ? tok : a.b - 1) * (A8 ? a.m : kb) + g * 16 * XN;
     }
-    // XL (per-token 4 x 4 tiles, K short enough): each wave copies its K slice of Q_X (its
+    // XL (per-token 16-block tiles, K short enough): each wave copies its K slice of Q_X (its
     // pieces x FM token tiles, 1 KB a block) into its own part of the LDS that the
     // cross-wave reduction fills afterwards, by direct-to-LDS loads issued ahead of the
     // weight stream; the main loop then reads X from LDS and only the weights stream from
@@ -491,10 +491,11 @@ static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
                                dim3(NWA * 64), 0, stream, a);
         return hipGetLastError();
     }
-    // per-token 4 x 4 tiles with every wave's K slice of Q_X within its part of the LDS
-    // reduction buffer: X read from LDS (measured on MI355X: +8-11% at 49-64 tokens,
-    // m = 4096; no gain on 8 x 2 tiles)
-    constexpr bool XLT = FN == 4 && FM == 4;
+    // per-token 16-block tiles with every wave's K slice of Q_X within its part of the LDS
+    // reduction buffer: X read from LDS (measured on MI355X, Y bitwise equal: 4 x 4 blocks
+    // at 49-64 tokens and m <= 4096 21-25% faster, 8 x 2 blocks at 27-32 tokens and
+    // m = 8192 6-9% faster)
+    constexpr bool XLT = FN * FM >= 16;
     const bool xl = XLT && (a.m / 128 + NW - 1) / NW <= FN;
     if (a.acc) {
         if (xl)
