@@ -88,7 +88,13 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
     static_assert(!(GRP && A8), "group-wise scales with 4-bit activations only");
     constexpr int XN = A8 ? 2 : 1;       // 16-byte loads per token row per piece
     constexpr int SH = A8 ? 4 : 8;       // log2 of the operands' combined scale
-    __shared__ v4i red[NW][FN * FM][kWave];
+    // LDS: the cross-wave reduction buffer red[NW][FN*FM][kWave]; with XL it also holds
+    // each wave's K slice of Q_X (XSLICE bytes a wave) during the main loop
+    constexpr int XSLICE = !XL ? 0 : FN * FM * 1024 > 131072 / NW ? FN * FM * 1024 : 131072 / NW;
+    constexpr int RED_V4 = NW * FN * FM * kWave;
+    constexpr int LDS_V4 = NW * XSLICE / 16 > RED_V4 ? NW * XSLICE / 16 : RED_V4;
+    __shared__ v4i red_lds[LDS_V4];
+    v4i (*const red)[FN * FM][kWave] = reinterpret_cast<v4i (*)[FN * FM][kWave]>(red_lds);
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int li = lane & 15, g = lane >> 4;
     // GRP: neighbouring channel tiles on one XCD, so the two halves of a 128-byte line of
@@ -112,16 +118,18 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
         const int64_t tok = fm * 16 + li;
         xrow[fm] = a.qx + (tok < a.b ? tok : a.b - 1) * (A8 ? a.m : kb) + g * 16 * XN;
     }
-    // XL (per-token 16-block tiles, K short enough): each wave copies its K slice of Q_X (its
-    // pieces x FM token tiles, 1 KB a block) into its own part of the LDS that the
-    // cross-wave reduction fills afterwards, by direct-to-LDS loads issued ahead of the
-    // weight stream; the main loop then reads X from LDS and only the weights stream from
-    // memory. Lane l of the copy of block (piece c, tile fm) fetches bytes 64 c + 16 (l % 4)
-    // of token row 16 fm + l / 4, so a block holds 64-byte rows in token order, read back
-    // by lane (li, g) at 64 li + 16 g. The launcher picks XL only where a wave's slice fits
-    // its part of red: at most FN pieces a wave, ceil(m / 128 / NW) <= FN.
-    static_assert(!XL || (!GRP && !A8 && FN * FM >= 16), "X slices in LDS: pipelined per-token tiles");
-    uint8_t *const xls = reinterpret_cast<uint8_t *>(&red[wave][0][0]);
+    // XL (K short enough): each wave copies its K slice of Q_X (its pieces x FM token tiles,
+    // 1 KB a block) into its own XSLICE bytes of that LDS by direct-to-LDS loads issued
+    // ahead of the weight stream; the main loop then reads X from LDS and only the weights
+    // (and group scales) stream from memory. Lane l of the copy of block (piece c, tile fm)
+    // fetches bytes 64 c + 16 (l % 4) of token row 16 fm + l / 4, so a block holds 64-byte
+    // rows in token order, read back by lane (li, g) at 64 li + 16 g. The launcher picks XL
+    // only where a wave's slice fits: ceil(m / 128 / NW) FM KB <= XSLICE. Where XSLICE is
+    // the wave's own part of red (16-block tiles of eight waves) the wave overwrites only
+    // its own slice when it stores its partial sums; otherwise the CTA meets at a barrier
+    // first.
+    static_assert(!XL || !A8, "X slices in LDS: 4-bit activations");
+    uint8_t *const xls = reinterpret_cast<uint8_t *>(red_lds) + wave * XSLICE;
 
     // Epilogue tiles are dealt to the waves in turn (tile t to wave t % NW). When a
     // wave owns one tile, its low-rank operands are loaded here, ahead of the main
@@ -280,8 +288,9 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
                 // the copy of X first, then the first batch's weights; once at most those
                 // weight loads are outstanding the copy has landed and X is read from LDS
                 copy_x();
+                asm volatile("" ::: "memory");  // the copy stays ahead of the weight loads
                 load_batch(cb, ba, false);
-                wait_vmcnt<U * FN>();
+                wait_vmcnt<U * (GRP ? 2 * FN + FM : FN)>();
                 asm volatile("" ::: "memory");
 #pragma unroll
                 for (int u = 0; u < U; ++u) load_x(cb + u < ce ? cb + u : ce - 1, ba.bx[u]);
@@ -301,16 +310,37 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
         }
     } else {
         int64_t c = cb;
+        if constexpr (XL) {
+            if (cb < ce) copy_x();
+            asm volatile("" ::: "memory");  // the copy stays ahead of the weight loads
+        }
         for (; c + U <= ce; c += U) {
             uint4 bw[U][FN], bx[U][FM][XN];
             float4 sw4[U][GRP ? FN : 1];
             float sx1[U][GRP ? FM : 1];
+            if constexpr (XL) {
+                // weights (and scales) of the batch first; at the first batch, once at most
+                // those loads are outstanding the copy of X has landed
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+                for (int u = 0; u < U; ++u) {
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn) bw[u][fn] = load_stream16(wrow[fn] + (c - cb + u) * kPanelPiece);
-                load_x(c + u, bx[u]);
-                load_scales(c + u, sw4[u], sx1[u]);
+                    for (int fn = 0; fn < FN; ++fn) bw[u][fn] = load_stream16(wrow[fn] + (c - cb + u) * kPanelPiece);
+                    load_scales(c + u, sw4[u], sx1[u]);
+                }
+                if (c == cb) {
+                    wait_vmcnt<U * (GRP ? 2 * FN + FM : FN)>();
+                    asm volatile("" ::: "memory");
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) load_x(c + u, bx[u]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) bw[u][fn] = load_stream16(wrow[fn] + (c - cb + u) * kPanelPiece);
+                    load_x(c + u, bx[u]);
+                    load_scales(c + u, sw4[u], sx1[u]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of its first use
 #pragma unroll
@@ -322,8 +352,17 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
             float sx1[GRP ? FM : 1];
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) bw[fn] = load_stream16(wrow[fn] + (c - cb) * kPanelPiece);
-            load_x(c, bx);
-            load_scales(c, sw4, sx1);
+            if constexpr (XL) {
+                load_scales(c, sw4, sx1);
+                if (c == cb) {  // no whole batch before: wait for the copy of X here
+                    wait_vmcnt<GRP ? 2 * FN + FM : FN>();
+                    asm volatile("" ::: "memory");
+                }
+                load_x(c, bx);
+            } else {
+                load_x(c, bx);
+                load_scales(c, sw4, sx1);
+            }
             mma(bw, bx, sw4, sx1);
         }
     }
@@ -356,6 +395,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
         }
     }
 
+    if constexpr (XL && XSLICE != FN * FM * 1024) __syncthreads();  // every wave done with its slice of X
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -491,12 +531,17 @@ static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
                                dim3(NWA * 64), 0, stream, a);
         return hipGetLastError();
     }
-    // per-token 16-block tiles with every wave's K slice of Q_X within its part of the LDS
-    // reduction buffer: X read from LDS (measured on MI355X, Y bitwise equal: 4 x 4 blocks
-    // at 49-64 tokens and m <= 4096 21-25% faster, 8 x 2 blocks at 27-32 tokens and
-    // m = 8192 6-9% faster)
-    constexpr bool XLT = FN * FM >= 16;
-    const bool xl = XLT && (a.m / 128 + NW - 1) / NW <= FN;
+    // X read from LDS (XL) where it measured faster on MI355X (Y bitwise equal): per-token
+    // tiles of 16 blocks whose waves' K slices of Q_X fit their parts of the reduction
+    // buffer (4 x 4 blocks at 49-64 tokens and m <= 4096 21-25% faster, 8 x 2 blocks at
+    // 27-32 tokens and m = 8192 6-9%), and eight-wave tiles of 2 or 4 token blocks at
+    // m <= 4096 on at most 256 CTAs (6-8%; with 128 KB of LDS a CTA, larger grids lose a
+    // CTA per compute unit and ran 4-22% slower, as did m = 8192 and the group-wise loop)
+    constexpr bool XLT = FN * FM >= 16 || (NW == 8 && FM >= 2);
+    constexpr int64_t XSL = !XLT ? 0 : FN * FM * 1024 > 131072 / NW ? FN * FM * 1024 : 131072 / NW;
+    const int64_t xpieces = (a.m / 128 + NW - 1) / NW;  // most pieces a wave streams
+    const bool xl = XLT && xpieces * FM * 1024 <= XSL &&
+                    (FN * FM >= 16 || (a.m <= 4096 && (int64_t)grid.x <= 256));
     if (a.acc) {
         if (xl)
             hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true, 1, NW, false, false, XLT>), grid, dim3(NW * 64), 0,
