@@ -90,7 +90,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
     constexpr int SH = A8 ? 4 : 8;       // log2 of the operands' combined scale
     // LDS: the cross-wave reduction buffer red[NW][FN*FM][kWave]; with XL it also holds
     // each wave's K slice of Q_X (XSLICE bytes a wave) during the main loop
-    constexpr int XSLICE = !XL ? 0 : FN * FM * 1024 > 131072 / NW ? FN * FM * 1024 : 131072 / NW;
+    constexpr int XSLICE = !XL ? 0 : FN * FM * 1024 > 16384 ? FN * FM * 1024 : 16384;
     constexpr int RED_V4 = NW * FN * FM * kWave;
     constexpr int LDS_V4 = NW * XSLICE / 16 > RED_V4 ? NW * XSLICE / 16 : RED_V4;
     __shared__ v4i red_lds[LDS_V4];
@@ -531,17 +531,19 @@ static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
                                dim3(NWA * 64), 0, stream, a);
         return hipGetLastError();
     }
-    // X read from LDS (XL) where it measured faster on MI355X (Y bitwise equal): per-token
-    // tiles of 16 blocks whose waves' K slices of Q_X fit their parts of the reduction
-    // buffer (4 x 4 blocks at 49-64 tokens and m <= 4096 21-25% faster, 8 x 2 blocks at
-    // 27-32 tokens and m = 8192 6-9%), and eight-wave tiles of 2 or 4 token blocks at
-    // m <= 4096 on at most 256 CTAs (6-8%; with 128 KB of LDS a CTA, larger grids lose a
-    // CTA per compute unit and ran 4-22% slower, as did m = 8192 and the group-wise loop)
-    constexpr bool XLT = FN * FM >= 16 || (NW == 8 && FM >= 2);
-    constexpr int64_t XSL = !XLT ? 0 : FN * FM * 1024 > 131072 / NW ? FN * FM * 1024 : 131072 / NW;
+    // X read from LDS (XL) where it measured faster on MI355X (Y bitwise equal), each wave's
+    // K slice of Q_X fitting its XSL bytes: per-token tiles of 16 blocks (4 x 4 at 49-64
+    // tokens and m <= 4096 21-25% faster, 8 x 2 at 27-32 tokens and m = 8192 6-9%); per-token
+    // tiles of 2 or 4 token blocks at m <= 4096, eight-wave ones (128 KB of LDS, one CTA a
+    // compute unit) on at most 256 CTAs (4-8%; larger grids 4-22% slower, as was m = 8192);
+    // group-wise tiles at m <= 4096 (4-12%). Per-token tiles of one token block ran 1-5%
+    // slower and stay on global loads.
+    constexpr bool XLT = FN * FM >= 16 || FM >= 2;
+    constexpr int64_t XSL = FN * FM * 1024 > 16384 ? FN * FM * 1024 : 16384;
     const int64_t xpieces = (a.m / 128 + NW - 1) / NW;  // most pieces a wave streams
     const bool xl = XLT && xpieces * FM * 1024 <= XSL &&
-                    (FN * FM >= 16 || (a.m <= 4096 && (int64_t)grid.x <= 256));
+                    (FN * FM >= 16 || (a.m <= 4096 && (NW == 4 || (int64_t)grid.x <= 256)));
+    const bool xlg = (a.m / 128 + 3) / 4 * FM * 1024 <= XSL && a.m <= 4096;  // group-wise: four waves
     if (a.acc) {
         if (xl)
             hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true, 1, NW, false, false, XLT>), grid, dim3(NW * 64), 0,
@@ -550,7 +552,10 @@ static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, 0, true, 1, NW>), grid, dim3(NW * 64), 0, stream, a);
     } else if (a.group && tk) {
         if constexpr (TKS) launch_decode_tk<FN, FM, UG, RS, 4, true, false>(a, grid, stream);
-    } else if (a.group)
+    } else if (a.group && xlg)
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, 1, 4, true, false, true>), grid, dim3(256), 0,
+                           stream, a);
+    else if (a.group)
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, 1, 4, true>), grid, dim3(256), 0, stream, a);
     else if (tk) {
         if constexpr (TKS) launch_decode_tk<FN, FM, UT, RS, NWT, false, false>(a, grid, stream);
