@@ -290,6 +290,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
                 copy_x();
                 asm volatile("" ::: "memory");  // the copy stays ahead of the weight loads
                 load_batch(cb, ba, false);
+                asm volatile("" ::: "memory");  // every load of the batch issued before the wait
                 wait_vmcnt<U * (GRP ? 2 * FN + FM : FN)>();
                 asm volatile("" ::: "memory");
 #pragma unroll
@@ -328,6 +329,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
                     load_scales(c + u, sw4[u], sx1[u]);
                 }
                 if (c == cb) {
+                    asm volatile("" ::: "memory");  // every load of the batch issued before the wait
                     wait_vmcnt<U * (GRP ? 2 * FN + FM : FN)>();
                     asm volatile("" ::: "memory");
                 }
@@ -355,6 +357,7 @@ __global__ __launch_bounds__(NW * 64) void dual_linear_decode(DualArgs a) {
             if constexpr (XL) {
                 load_scales(c, sw4, sx1);
                 if (c == cb) {  // no whole batch before: wait for the copy of X here
+                    asm volatile("" ::: "memory");
                     wait_vmcnt<GRP ? 2 * FN + FM : FN>();
                     asm volatile("" ::: "memory");
                 }
