@@ -75,6 +75,8 @@ SHAPES = [
     (16, 512, 16384, 16), (5, 2048, 16384, 64), (300, 4096, 1040, 32), (27, 512, 8208, 48),
     # wide few-token grids: 2x2 and 4x4 blocks of 16 per CTA, a partial last channel tile
     (27, 384, 24592, 32), (64, 256, 12304, 48), (48, 512, 8192, 32),
+    # tilings that read Q_X from LDS at m <= 4096: 2x1, 2x2 and 4x4 blocks, ragged tokens
+    (9, 2048, 8192, 32), (30, 3072, 24576, 32), (61, 640, 12304, 16),
 ]
 
 

@@ -140,6 +140,10 @@ RAGGED = [
     # 4x4-block CTAs whose waves read their K slices of Q_X from LDS (a full slice of
     # four pieces a wave; a ragged token count and a partial last channel tile)
     (64, 4096, 14336, 64), (49, 2048, 12304, 32),
+    # the other tilings that read Q_X from LDS, each with ragged tokens and uneven pieces
+    # per wave: 1x2 and 1x4 blocks of eight waves, 2x4, 2x2 of four waves, 8x2 at m = 8192
+    (20, 1536, 1040, 32), (40, 3072, 2000, 48), (57, 2560, 6160, 16), (31, 4096, 9008, 64),
+    (50, 1152, 12304, 32), (29, 8192, 24592, 32),
 ]
 
 
