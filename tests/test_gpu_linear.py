@@ -42,7 +42,8 @@ def _run(d):
 # channel tiles per CTA), the decode shapes that need T whole, and many tokens
 SHAPES = [(16, 4096, 4096, 32), (16, 512, 512, 16), (1, 4096, 272, 32), (5, 2048, 16384, 64),
           (16, 8192, 1024, 128), (24, 4096, 4096, 32), (32, 1024, 8192, 64), (48, 2048, 512, 16),
-          (64, 4096, 2048, 32), (200, 1024, 528, 48), (16, 4096, 4096, 0), (3, 16384, 256, 256)]
+          (64, 4096, 2048, 32), (200, 1024, 528, 48), (16, 4096, 4096, 0), (3, 16384, 256, 256),
+          (29, 4096, 12304, 32)]  # 2x2 blocks reading Q_X from LDS with T's slices in the epilogue
 
 
 @pytest.mark.parametrize("b,m,n,r", SHAPES)

@@ -504,12 +504,20 @@ constexpr int halved(int u) { return u > 4 ? u / 2 : u; }
 // at most kMaxTSlices / RS) that hold them. Its epilogue loads every slice it is built
 // for before the main loop, so unused slices would cost (measured on the o_proj shape:
 // 16 slices for 8 used, +0.9 us).
+// xl: read X from LDS (per-token 2 x 2 blocks only: 7-8% faster there with T's slices in
+// the epilogue, measured on MI355X; 1 x 2 blocks 3% slower, 1 x 4 and group-wise +2-3%)
 template <int FN, int FM, int U, int RS, int NWT, bool GRP, bool A8, int TK = 2>
-static void launch_decode_tk(const DualArgs &a, const dim3 grid, hipStream_t stream) {
+static void launch_decode_tk(const DualArgs &a, const dim3 grid, hipStream_t stream, bool xl = false) {
     if constexpr (2 * TK * RS <= kMaxTSlices) {
-        if (a.tks > TK) return launch_decode_tk<FN, FM, U, RS, NWT, GRP, A8, 2 * TK>(a, grid, stream);
+        if (a.tks > TK) return launch_decode_tk<FN, FM, U, RS, NWT, GRP, A8, 2 * TK>(a, grid, stream, xl);
     }
-    hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false, TK, NWT, GRP, A8>), grid, dim3(NWT * 64), 0, stream, a);
+    constexpr bool XLK = !GRP && !A8 && FN == 2 && FM == 2;
+    if (XLK && xl)
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false, TK, NWT, GRP, A8, XLK>), grid, dim3(NWT * 64), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false, TK, NWT, GRP, A8>), grid, dim3(NWT * 64), 0, stream,
+                           a);
 }
 
 template <int FN, int FM, int U, int NW, int RS>
@@ -561,7 +569,9 @@ static hipError_t launch_decode_rs(const DualArgs &a, hipStream_t stream) {
     else if (a.group)
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, UG, RS, false, 1, 4, true>), grid, dim3(256), 0, stream, a);
     else if (tk) {
-        if constexpr (TKS) launch_decode_tk<FN, FM, UT, RS, NWT, false, false>(a, grid, stream);
+        if constexpr (TKS)
+            launch_decode_tk<FN, FM, UT, RS, NWT, false, false>(
+                a, grid, stream, (a.m / 128 + NWT - 1) / NWT * FM * 1024 <= 16384 && a.m <= 4096);
     } else if (xl)
         hipLaunchKernelGGL((dual_linear_decode<FN, FM, U, RS, false, 1, NW, false, false, XLT>), grid, dim3(NW * 64), 0,
                            stream, a);
