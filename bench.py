@@ -1,16 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the fused W4A4 + low-rank linear on one MI355X.
 
-One step = one call of the layer on one batch: twq_quantize_act (per-token
-quantization + T = X L1) then twq_dual_linear (residual int4 GEMM + low-rank
-epilogue), weights pre-packed and resident in HBM. Inputs are synthetic (seeded,
+One step = one call of the layer on one batch: twq_linear (per-token quantization
++ T = X L1, then the residual int4 GEMM with the low-rank epilogue), weights
+pre-packed and resident in HBM. The default workload is the largest layer that
+fits one GPU, the 70B-size MLP gate/up layer at prefill (b=8192, m=8192,
+n=28672, r=128). Inputs are synthetic (seeded,
 with the shapes and value distributions of the layer configurations), and the
 steps rotate over enough copies of the weights that the caches (4 MB L2 per
 XCD, 256 MB Infinity Cache) cannot hold the working set.
 
 Prints one JSON line. `value` is effective TOPS = (2bmn + 2br(m+n)) / time per
-step. The `roofline` object prices the dominant kernel (twq_dual_linear)
-against HBM bandwidth (few tokens) or the int8 matrix-core peak (many tokens).
+step. The `roofline` object prices the dominant kernel -- the fused main-loop
+launch exactly as the timed call runs it, timed alone through the measurement
+export twq_debug_linear_main -- against HBM bandwidth (few tokens) or the int8
+matrix-core peak (many tokens).
 """
 from __future__ import annotations
 
@@ -104,6 +108,39 @@ def measured_traffic(workload):
         return None
     entry = rec.get("workloads", {}).get(workload)
     return None if entry is None else entry.get("traffic_bytes")
+
+
+def cpu_model():
+    """The host CPU's model name (the first "model name" of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def rocm_version():
+    """The ROCm release of the image (/opt/rocm/.info/version), or None."""
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                return f.read().strip()
+        except OSError:
+            continue
+    return None
+
+
+def host_env(torch):
+    """Where the numbers were taken: GPU name, ROCm and HIP versions, torch, host CPU."""
+    try:
+        gpu = torch.cuda.get_device_name(0)
+    except Exception:  # noqa: BLE001 - informative only
+        gpu = None
+    return {"gpu": gpu, "rocm": rocm_version(), "hip": getattr(torch.version, "hip", None),
+            "torch": torch.__version__, "host_cpu": cpu_model(), "host_threads": os.cpu_count()}
 
 
 def lowrank_storage_ratio(m, n, r):
@@ -342,7 +379,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="o_proj_decode")
+    ap.add_argument("--config", default="70b_gate_up_prefill")
     ap.add_argument("--path", choices=("linear", "split"), default="linear",
                     help="linear: one twq_linear call per step; split: twq_quantize_act + twq_dual_linear")
     ap.add_argument("--lowrank", choices=("fp16", "int4"), default="fp16",
@@ -485,16 +522,36 @@ def main():
     def hs():
         return twq.ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
+    def layer_main(s, stream):
+        # the fused launch of the one-call layer alone, on the Q_X, s_X and T (or T's
+        # partial sums) that an earlier call of the same shape left in the workspace
+        if a8:
+            twq._check(L.twq_debug_linear_a8_main(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["l1t"]), P(s["l2t"]), r,
+                                                  P(s["y"]), b, m, n, P(ws), wsb, stream), "twq_debug_linear_a8_main")
+        elif grp:
+            twq._check(L.twq_debug_linear_grouped_main(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["l1t"]), P(s["l2t"]),
+                                                       r, P(s["y"]), b, m, n, grp, P(ws), wsb, stream),
+                       "twq_debug_linear_grouped_main")
+        else:
+            twq._check(L.twq_debug_linear_main(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["l1t"]), P(s["l2t"]), r,
+                                               P(s["y"]), b, m, n, P(ws), wsb, stream), "twq_debug_linear_main")
+
+    one_call = args.path == "linear" and not lr4
+
     def steps_fn(k, with_quant=True, offset=0):
-        # with_quant=False: the main-loop kernel alone (twq_dual_linear on the Q_X,
-        # s_X and T of an earlier call), for its launch duration
+        # with_quant=False: the main-loop kernel alone, exactly as the timed step
+        # launches it (the one-call layer's fused launch, or twq_dual_linear of the
+        # split path), for its launch duration
         def run():
             st = hs()
             for i in range(k):
                 s = sets[(i + offset) % copies]
                 if not with_quant:
-                    dual(s, st)
-                elif args.path == "linear" and not lr4:
+                    if one_call:
+                        layer_main(s, st)
+                    else:
+                        dual(s, st)
+                elif one_call:
                     layer(s, st)
                 else:
                     quant(s, st)
@@ -557,15 +614,15 @@ def main():
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         ach = 2 * b * m * n / (us_dual * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                 "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": traffic}
-    roof["kernel"] = ("twq_dual_linear_lr4" if lr4 else "twq_dual_linear_grouped" if grp else
-                      "twq_dual_linear_a8" if a8 else "twq_dual_linear")
+    sfx = "_grouped" if grp else "_a8" if a8 else ""
+    roof["kernel"] = ("twq_dual_linear_lr4" if lr4 else f"fused launch of twq_linear{sfx}" if one_call
+                      else f"twq_dual_linear{sfx}")
     roof["kernel_us"] = round(us_dual, 3)
     roof["algorithmic_bytes"] = kbytes
     roof["algorithmic_int8_ops"] = 2 * b * m * n
 
-    sfx = "_grouped" if grp else "_a8" if a8 else ""
     if lr4:
         entry_points = "twq_quantize_act+twq_lowrank_requant+twq_dual_linear_lr4"
     elif args.path == "linear":
@@ -594,14 +651,17 @@ def main():
                    "entry_points": entry_points,
                    "call_bytes": cbytes,
                    "hbm_frac_whole_call": round(cbytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                   "int8_mfma_frac_whole_call": round(2 * b * m * n / (ms_step * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)},
+                   "int8_mfma_frac_whole_call": round(2 * b * m * n / (ms_step * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                   "seed": {"seed_sequence": synth.SEED_BASE, "spawn_key": cfg.index, "generator": "PCG64",
+                            "synth_version": synth.GEN_VERSION}},
+        "env": host_env(torch),
         "roofline": roof,
     }
     if not args.no_cpu:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = (_cpu_baseline_grouped(d, grp) if grp else _cpu_baseline_a8(d) if a8
                                else _cpu_baseline(d, lr4=lr4))
-        out["cpu_baseline"]["host"] = platform.processor() or platform.machine()
+        out["cpu_baseline"]["host"] = cpu_model()
     print(json.dumps(out), flush=True)
 
 

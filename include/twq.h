@@ -72,8 +72,10 @@ typedef enum {
 /* Human-readable name of a status code (static storage). */
 const char *twq_status_string(int status);
 
-/* Text of the last TWQ_ERR_HIP on the calling thread ("" if none). */
+/* Text of the last TWQ_ERR_HIP on the calling thread ("" if none). The two names
+ * return the same per-thread string. */
 const char *twq_last_error_string(void);
+const char *twq_last_hip_error(void);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int twq_version(void);
@@ -160,6 +162,19 @@ twq_status twq_linear(const void *x, const void *qw, const float *sw, const void
                       size_t workspace_bytes, void *stream);
 
 /*
+ * Measurement export: the second launch of twq_linear alone -- the fused main loop
+ * and epilogue, with exactly the kernel, grid and arguments twq_linear uses for this
+ * shape -- reading Q_X, s_X and T (or T's partial sums over K slices) from a
+ * workspace that a twq_linear call with the same b, m, n and r has filled. Its
+ * duration is the duration of that launch inside twq_linear. Arguments, checks and
+ * errors are those of twq_linear; x and l1t are validated but not read. On a
+ * workspace twq_linear has not filled for this shape, Y is unspecified.
+ */
+twq_status twq_debug_linear_main(const void *x, const void *qw, const float *sw, const void *l1t,
+                                 const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * ---- group-wise scales (TwinQuant page 1, section 5.1 and page 2, section 5.1:
  * weights and activations quantized group-wise, groups of 128) ----
  *
@@ -191,6 +206,11 @@ size_t twq_linear_grouped_workspace_bytes(int64_t b, int64_t m, int64_t n, int64
 twq_status twq_linear_grouped(const void *x, const void *qw, const float *sw, const void *l1t,
                               const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n,
                               int64_t g, void *workspace, size_t workspace_bytes, void *stream);
+/* Measurement export: the second launch of twq_linear_grouped alone (as twq_debug_linear_main). */
+twq_status twq_debug_linear_grouped_main(const void *x, const void *qw, const float *sw, const void *l1t,
+                                         const void *l2t, int64_t r, void *y, int64_t b, int64_t m,
+                                         int64_t n, int64_t g, void *workspace, size_t workspace_bytes,
+                                         void *stream);
 
 /*
  * ---- W4A8 (TwinQuant page 1, section 5.1: WxAy names x-bit weights and y-bit
@@ -214,6 +234,10 @@ size_t twq_linear_a8_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r)
 twq_status twq_linear_a8(const void *x, const void *qw, const float *sw, const void *l1t,
                          const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n,
                          void *workspace, size_t workspace_bytes, void *stream);
+/* Measurement export: the second launch of twq_linear_a8 alone (as twq_debug_linear_main). */
+twq_status twq_debug_linear_a8_main(const void *x, const void *qw, const float *sw, const void *l1t,
+                                    const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n,
+                                    void *workspace, size_t workspace_bytes, void *stream);
 /* Test export: the W4A8 main loop storing the exact int32 acc[i][j] = sum_k Q_X[i][k] Q_W[j][k]. */
 twq_status twq_debug_residual_acc_a8(const void *qx, const void *qw, int32_t *acc, int64_t b,
                                      int64_t m, int64_t n, void *stream);

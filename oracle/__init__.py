@@ -74,6 +74,8 @@ def _load():
         lib.orc_dual_linear_a8_sampled.restype = ctypes.c_int
         lib.orc_dual_linear_a8_sampled.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P]
         lib.orc_max_threads.restype = ctypes.c_int
+        lib.orc_require_i32.restype = ctypes.c_int64
+        lib.orc_require_i32.argtypes = [_I]
         _lib = lib
     return _lib
 
@@ -90,6 +92,20 @@ def _p(a):
 def _h(a):
     """fp16 array -> its uint16 bit pattern (the C side decodes the format itself)."""
     return np.ascontiguousarray(a, dtype=np.float16).view(np.uint16)
+
+
+FP16_MAX = 65504.0
+
+
+def _fp16_range(y, t=None):
+    """The layer stores Y in fp16 and feeds T to fp16 matrix cores, so the error budget
+    of the comparison assumes neither leaves the fp16 range; an input that breaks this
+    is rejected here, where Y and T are formed."""
+    if y.size and not np.abs(y).max() < FP16_MAX:
+        raise AssertionError(f"oracle Y reaches {np.abs(y).max():.6g}, outside the fp16 range")
+    if t is not None and t.size and not np.abs(t).max() < FP16_MAX:
+        raise AssertionError(f"oracle T reaches {np.abs(t).max():.6g}, outside the fp16 range")
+    return y
 
 
 def max_threads() -> int:
@@ -176,6 +192,7 @@ def dual_linear(x, w_res, l1t, l2t):
                                  _p(out["sw"]), _p(out["acc"]), _p(out["t"]), _p(out["y"]))
     if rc:
         raise MemoryError("oracle allocation failed")
+    _fp16_range(out["y"], out["t"])
     return out
 
 
@@ -197,7 +214,7 @@ def dual_linear_sampled(x, w_res, l1t, l2t, rows, cols):
                                          _p(rows), _p(cols), rows.shape[0], _p(acc), _p(y))
     if rc:
         raise MemoryError("oracle allocation failed")
-    return acc, y
+    return acc, _fp16_range(y)
 
 
 def quantize_lowrank(l1t, l2t):
@@ -251,6 +268,7 @@ def dual_linear_lr4(x, w_res, l1t, l2t):
                                      _p(out["acc2"]), _p(out["y"]))
     if rc:
         raise MemoryError("oracle allocation failed")
+    _fp16_range(out["y"])
     return out
 
 
@@ -273,7 +291,7 @@ def dual_linear_lr4_sampled(x, w_res, l1t, l2t, rows, cols):
                                              rows.shape[0], _p(acc), _p(acc2), _p(y))
     if rc:
         raise MemoryError("oracle allocation failed")
-    return acc, acc2, y
+    return acc, acc2, _fp16_range(y)
 
 
 def _check_group(m, g):
@@ -335,6 +353,7 @@ def dual_linear_grouped(x, w_res, l1t, l2t, g):
                                          _p(out["sw"]), _p(out["y"]))
     if rc:
         raise MemoryError("oracle allocation failed")
+    _fp16_range(out["y"])
     return out
 
 
@@ -357,7 +376,7 @@ def dual_linear_grouped_sampled(x, w_res, l1t, l2t, g, rows, cols):
                                                  _p(cols), rows.shape[0], _p(y))
     if rc:
         raise MemoryError("oracle allocation failed")
-    return y
+    return _fp16_range(y)
 
 
 def quantize_act_a8(x):
@@ -386,6 +405,7 @@ def dual_linear_a8(x, w_res, l1t, l2t):
                                     _p(out["qw_packed"]), _p(out["sw"]), _p(out["acc"]), _p(out["y"]))
     if rc:
         raise MemoryError("oracle allocation failed")
+    _fp16_range(out["y"])
     return out
 
 
@@ -408,7 +428,7 @@ def dual_linear_a8_sampled(x, w_res, l1t, l2t, rows, cols):
                                             rows.shape[0], _p(acc), _p(y))
     if rc:
         raise MemoryError("oracle allocation failed")
-    return acc, y
+    return acc, _fp16_range(y)
 
 
 def unpack_codes(packed):

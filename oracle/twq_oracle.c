@@ -44,11 +44,24 @@
  * example and stay a reading, not a pin.
  */
 #include <math.h>
+#include <stdio.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define Q_MAX 7 /* 2^(k-1) - 1 for k = 4 bits: TwinQuant page 1, section 2, eq. (1) */
+
+/* Every integer sum of the layer must fit the int32 accumulator of the matrix cores
+ * (|acc| < 2^31; with |q| <= 7 and m <= 131072 it is at most 49 m). The sums here are
+ * int64, so a violation is detected rather than wrapped: it aborts with a message. */
+int64_t orc_require_i32(int64_t v)
+{
+    if (v >= ((int64_t)1 << 31) || v <= -((int64_t)1 << 31)) {
+        fprintf(stderr, "twq_oracle: integer sum %lld outside the int32 accumulator range\n", (long long)v);
+        abort();
+    }
+    return v;
+}
 
 /* IEEE 754 binary16 -> binary64, straight from the format's definition:
  * sign 1 bit, exponent 5 bits (bias 15), fraction 10 bits. */
@@ -150,7 +163,7 @@ void orc_residual_acc(const int8_t *qx, const int8_t *qw, int64_t b, int64_t m, 
             int64_t sum = 0;
             for (int64_t k = 0; k < m; k++)
                 sum += (int64_t)qx[i * m + k] * (int64_t)qw[j * m + k];
-            acc[i * n + j] = sum;
+            acc[i * n + j] = orc_require_i32(sum);
         }
 }
 
@@ -262,7 +275,7 @@ int orc_dual_linear_sampled(const uint16_t *x, const float *w_res, const uint16_
                 tu += orc_half_to_double(x[i * m + k]) * orc_half_to_double(l1t[u * m + k]);
             lr += tu * orc_half_to_double(l2t[j * r + u]);
         }
-        acc_out[p] = acc;
+        acc_out[p] = orc_require_i32(acc);
         y_out[p] = (double)sxi * (double)swj * (double)acc + lr;
         free(xr); free(qx); free(qw);
     }
@@ -324,6 +337,7 @@ void orc_lowrank_requant(const int8_t *qx, const float *sx, const int8_t *ql1, c
             int64_t hi = 0;
             for (int64_t k = 0; k < m; k++)
                 hi += (int64_t)qx[i * m + k] * (int64_t)ql1[t * m + k];
+            orc_require_i32(hi);
             if (h_out)
                 h_out[i * r + t] = hi;
             float prod = sx[i] * (float)hi; /* (s_X H) first ... */
@@ -369,8 +383,9 @@ int orc_dual_linear_lr4(const uint16_t *x, const float *w_res, const uint16_t *l
                 acc += (int64_t)qx[i * m + k] * (int64_t)qw[j * m + k];
             for (int64_t t = 0; t < r; t++)
                 acc2 += (int64_t)qh[i * r + t] * (int64_t)ql2[j * r + t];
+            orc_require_i32(acc);
             if (acc2_out)
-                acc2_out[i * n + j] = acc2;
+                acc2_out[i * n + j] = orc_require_i32(acc2);
             y[i * n + j] = (double)sx[i] * (double)sw[j] * (double)acc + (double)sh[i] * (double)acc2;
         }
     if (sh_out)
@@ -421,8 +436,8 @@ int orc_dual_linear_lr4_sampled(const uint16_t *x, const float *w_res, const uin
             acc += (int64_t)qx[k] * (int64_t)qw[k];
         for (int64_t t = 0; t < r; t++)
             acc2 += (int64_t)qh[t] * (int64_t)ql2[j * r + t];
-        acc_out[p] = acc;
-        acc2_out[p] = acc2;
+        acc_out[p] = orc_require_i32(acc);
+        acc2_out[p] = orc_require_i32(acc2);
         y_out[p] = (double)sxi * (double)swj * (double)acc + (double)shi * (double)acc2;
         free(xr); free(qx); free(qw); free(qh);
     }
@@ -525,7 +540,7 @@ int orc_dual_linear_a8_sampled(const uint16_t *x, const float *w_res, const uint
                 tu += orc_half_to_double(x[i * m + k]) * orc_half_to_double(l1t[u * m + k]);
             lr += tu * orc_half_to_double(l2t[j * r + u]);
         }
-        acc_out[p] = acc;
+        acc_out[p] = orc_require_i32(acc);
         y_out[p] = (double)sxi * (double)swj * (double)acc + lr;
         free(xr); free(qx); free(qw);
     }
@@ -603,7 +618,7 @@ void orc_residual_acc_grouped(const int8_t *qx, const int8_t *qw, int64_t b, int
                 int64_t sum = 0;
                 for (int64_t k = G * g; k < (G + 1) * g; k++)
                     sum += (int64_t)qx[i * m + k] * (int64_t)qw[j * m + k];
-                acc[(i * n + j) * ng + G] = sum;
+                acc[(i * n + j) * ng + G] = orc_require_i32(sum);
             }
 }
 
@@ -681,7 +696,7 @@ int orc_dual_linear_grouped_sampled(const uint16_t *x, const float *w_res, const
             int64_t acc = 0;
             for (int64_t k = G * g; k < (G + 1) * g; k++)
                 acc += (int64_t)qx[k] * (int64_t)qw[k];
-            y += (double)sxi[G] * (double)swj[G] * (double)acc;
+            y += (double)sxi[G] * (double)swj[G] * (double)orc_require_i32(acc);
         }
         double lr = 0.0;
         for (int64_t u = 0; u < r; u++) {

@@ -156,6 +156,23 @@ def split_lowrank(w_nm: np.ndarray, r: int, method: str, rng=None):
     return l1t, l2t, w_res
 
 
+FP16_MAX = 65504.0
+
+
+def check_fp16_headroom(x: np.ndarray, w_nm: np.ndarray, l1t: np.ndarray):
+    """Reject inputs whose unquantized products could leave the fp16 range.
+
+    By Cauchy-Schwarz, |X_i . W_j| <= |X_i| |W_j| and |X_i . L1_t| <= |X_i| |L1_t|
+    (Euclidean norms of rows), so max row norms bound every output of X W and every
+    T = X L1 without forming either. The layer stores Y in fp16 and feeds T to fp16
+    matrix cores; the quantized Y itself is checked where it is formed (the oracle)."""
+    xn = np.sqrt(np.square(x.astype(np.float64)).sum(axis=1)).max(initial=0.0)
+    wn = np.sqrt(np.square(w_nm.astype(np.float64)).sum(axis=1)).max(initial=0.0)
+    ln = np.sqrt(np.square(l1t.astype(np.float64)).sum(axis=1)).max(initial=0.0)
+    assert xn * wn < FP16_MAX, f"|X W| may reach {xn * wn:.6g}, outside the fp16 range"
+    assert xn * ln < FP16_MAX, f"|X L1| may reach {xn * ln:.6g}, outside the fp16 range"
+
+
 def make_layer(cfg: LayerConfig | str, seed_base: int = SEED_BASE, b: int | None = None,
                keep_w: bool = False):
     """All inputs of one configuration, deterministic in (config index, seed_base).
@@ -170,6 +187,7 @@ def make_layer(cfg: LayerConfig | str, seed_base: int = SEED_BASE, b: int | None
     x = np.ascontiguousarray(x[:bb])
     w = draw_w(rw, rwo, cfg.n, cfg.m, cfg.w_outlier_frac, cfg.w_outlier_scale)
     l1t, l2t, w_res = split_lowrank(w, cfg.r, cfg.svd, rsvd)
+    check_fp16_headroom(x, w, l1t)
     out = {"x": x, "w_res": w_res, "l1t": np.ascontiguousarray(l1t),
            "l2t": np.ascontiguousarray(l2t), "cfg": cfg}
     if keep_w:

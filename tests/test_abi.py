@@ -179,3 +179,4 @@ def test_panel_layout_helpers_follow_the_documented_offsets():
             flat[((j // 16) * (m // 128) + t // 64) * 1024 + (j % 16) * 64 + t % 64] = rows[j, t]
     assert np.array_equal(to_panels(rows).reshape(-1), flat)
     assert np.array_equal(from_panels(to_panels(rows)), rows)
+

@@ -15,6 +15,8 @@ import pytest
 import synth
 from tests import ratmodel
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -629,3 +631,47 @@ def test_fold_identity_and_rank_zero(oracle_lib):
     np.testing.assert_allclose(proj @ l1t.T.astype(np.float64), l1t.T.astype(np.float64), atol=2e-3)
     l1t0, l2t0, w_res0 = oracle_lib.fold_split(w, 0, None, None)
     assert l1t0.shape == (0, 32) and l2t0.shape == (24, 0) and (w_res0 == w).all()
+
+
+# ---- range guards of the error budget (the int32 accumulator, the fp16 outputs) ----
+
+def test_require_i32_accepts_the_accumulator_range(oracle_lib):
+    lib = oracle_lib._load()
+    for v in (0, 1, -1, 49 * 131072, -(49 * 131072), (1 << 31) - 1, -(1 << 31) + 1):
+        assert lib.orc_require_i32(v) == v
+
+
+@pytest.mark.parametrize("v", [1 << 31, -(1 << 31), 1 << 40])
+def test_require_i32_aborts_outside_int32(oracle_lib, v):
+    """An integer sum the int32 accumulator could not hold stops the oracle (in a child
+    process, so the abort does not take the test runner with it)."""
+    import subprocess
+    import sys
+    code = ("import oracle; oracle._load().orc_require_i32(%d); print('returned')" % v)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode != 0 and "returned" not in r.stdout
+    assert "outside the int32 accumulator range" in r.stderr
+
+
+def test_oracle_rejects_outputs_beyond_fp16(oracle_lib):
+    """A layer whose exact output exceeds the fp16 range is refused where Y is formed."""
+    x = np.zeros((1, 128), np.float16)
+    x[0, 0] = 60000.0
+    w = np.zeros((16, 128), np.float32)
+    w[0, 0] = 2.0  # Y[0][0] ~ 1.2e5
+    with pytest.raises(AssertionError, match="fp16 range"):
+        oracle_lib.dual_linear(x, w, None, None)
+    w[0, 0] = 0.5  # Y[0][0] ~ 3e4: accepted
+    assert np.isfinite(oracle_lib.dual_linear(x, w, None, None)["y"]).all()
+
+
+def test_synth_headroom_check():
+    """The generator's Cauchy-Schwarz bound accepts the configs and rejects a layer whose
+    products could overflow fp16."""
+    import synth
+    d = synth.make_layer("tiny", keep_w=True)
+    synth.check_fp16_headroom(d["x"], d["w"], d["l1t"])
+    with pytest.raises(AssertionError, match="fp16 range"):
+        synth.check_fp16_headroom(d["x"], d["w"] * 1000.0, d["l1t"])
+    with pytest.raises(AssertionError, match="fp16 range"):
+        synth.check_fp16_headroom(d["x"], d["w"], d["l1t"] * 1000.0)

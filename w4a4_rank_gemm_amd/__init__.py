@@ -25,14 +25,15 @@ STATUS_NAMES = {0: "TWQ_OK", 1: "TWQ_ERR_NULL", 2: "TWQ_ERR_SHAPE", 3: "TWQ_ERR_
                 4: "TWQ_ERR_UNSUPPORTED", 5: "TWQ_ERR_HIP", 6: "TWQ_ERR_WORKSPACE"}
 
 # every symbol include/twq.h declares
-EXPORTS = ("twq_status_string", "twq_last_error_string", "twq_version",
+EXPORTS = ("twq_status_string", "twq_last_error_string", "twq_last_hip_error", "twq_version",
            "twq_quantize_act_workspace_bytes", "twq_quantize_act", "twq_pack_weight",
            "twq_dual_linear", "twq_debug_residual_acc", "twq_linear_workspace_bytes",
            "twq_linear", "twq_quantize_act_grouped", "twq_pack_weight_grouped", "twq_dual_linear_grouped",
            "twq_linear_grouped_workspace_bytes", "twq_linear_grouped", "twq_quantize_act_a8",
            "twq_dual_linear_a8", "twq_linear_a8_workspace_bytes", "twq_linear_a8", "twq_debug_residual_acc_a8",
            "twq_pack_lowrank_int4",
-           "twq_lowrank_requant", "twq_dual_linear_lr4")
+           "twq_lowrank_requant", "twq_dual_linear_lr4", "twq_debug_linear_main",
+           "twq_debug_linear_grouped_main", "twq_debug_linear_a8_main")
 
 GROUP = 128  # group size of the group-wise entry points
 
@@ -65,6 +66,8 @@ def lib() -> ctypes.CDLL:
                 L.twq_status_string.argtypes = [ctypes.c_int]
                 L.twq_last_error_string.restype = ctypes.c_char_p
                 L.twq_last_error_string.argtypes = []
+                L.twq_last_hip_error.restype = ctypes.c_char_p
+                L.twq_last_hip_error.argtypes = []
                 L.twq_version.restype = ctypes.c_int
                 L.twq_quantize_act_workspace_bytes.restype = _S
                 L.twq_quantize_act_workspace_bytes.argtypes = [_I, _I, _I]
@@ -106,6 +109,11 @@ def lib() -> ctypes.CDLL:
                 L.twq_lowrank_requant.argtypes = [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _P]
                 L.twq_dual_linear_lr4.restype = ctypes.c_int
                 L.twq_dual_linear_lr4.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P]
+                for nm in ("twq_debug_linear_main", "twq_debug_linear_a8_main"):
+                    getattr(L, nm).restype = ctypes.c_int
+                    getattr(L, nm).argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _S, _P]
+                L.twq_debug_linear_grouped_main.restype = ctypes.c_int
+                L.twq_debug_linear_grouped_main.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _P, _S, _P]
                 _lib = L
     return _lib
 

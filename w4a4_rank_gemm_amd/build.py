@@ -34,8 +34,20 @@ def compile_flags() -> list[str]:
     ]
 
 
-def _compile(src: str) -> str:
+def _stale(src: str, out: str) -> bool:
+    """True if out is missing or older than its source or any header it may include."""
+    if not os.path.exists(out):
+        return True
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".h")]
+    deps.append(os.path.join(ROOT, "include", "twq.h"))
+    t = os.path.getmtime(out)
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     out = os.path.join(OBJ, os.path.basename(src) + ".o")
+    if incremental and not _stale(src, out):
+        return out
     cmd = [hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -43,11 +55,12 @@ def _compile(src: str) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (incremental: only those older than their inputs) and link."""
     os.makedirs(OBJ, exist_ok=True)
     os.makedirs(os.path.dirname(LIB), exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, incremental), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,4 +73,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    import sys
+    build(verbose=True, incremental="--incremental" in sys.argv)

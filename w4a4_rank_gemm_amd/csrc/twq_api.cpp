@@ -120,15 +120,34 @@ twq_status dual_linear_impl(const void *qx, const float *sx, const void *qw, con
     return e == hipSuccess ? TWQ_OK : hip_fail(e, name);
 }
 
-twq_status linear_impl(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t, int64_t r,
-                       void *y, int64_t b, int64_t m, int64_t n, int group, void *workspace, size_t workspace_bytes,
-                       void *stream, const char *name, int a8 = 0) {
+}  // namespace
+
+namespace twq {
+
+int linear_check(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t, int64_t r,
+                 const void *y, int64_t b, int64_t m, int64_t n) {
     if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return TWQ_ERR_SHAPE;
     if (b == 0 || n == 0) return TWQ_OK;
     if (!x || !qw || !sw || !y) return TWQ_ERR_NULL;
     if (r > 0 && (!l1t || !l2t)) return TWQ_ERR_NULL;
     if (!aligned16(x) || !aligned16(qw) || !aligned16(sw) || !aligned16(y)) return TWQ_ERR_ALIGN;
     if (r > 0 && (!aligned16(l1t) || !aligned16(l2t))) return TWQ_ERR_ALIGN;
+    return TWQ_OK;
+}
+
+size_t linear_workspace(int64_t b, int64_t m, int64_t n, int64_t r, int group, int a8) {
+    if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return 0;
+    return linear_layout(b, m, n, r, group, a8).total;
+}
+
+// main_only: skip the activation launch and run the fused launch alone on the Q_X, s_X
+// and T (or T's partial sums) an earlier call of the same shape left in the workspace
+// (the measurement export twq_debug_linear_main).
+int linear_run(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t, int64_t r, void *y,
+               int64_t b, int64_t m, int64_t n, int group, void *workspace, size_t workspace_bytes, void *stream,
+               const char *name, int a8, bool main_only) {
+    const int st0 = linear_check(x, qw, sw, l1t, l2t, r, y, b, m, n);
+    if (st0 != TWQ_OK || b == 0 || n == 0) return st0;
     const LinearLayout L = linear_layout(b, m, n, r, group, a8);
     if (!workspace || workspace_bytes < L.total) return TWQ_ERR_WORKSPACE;
     if (!aligned16(workspace)) return TWQ_ERR_ALIGN;
@@ -148,7 +167,7 @@ twq_status linear_impl(const void *x, const void *qw, const float *sw, const voi
     act.keep_partials = L.direct;
     act.group = group;
     act.a8 = a8;
-    hipError_t e = twq::launch_act(act, L.plan, st);
+    hipError_t e = main_only ? hipSuccess : twq::launch_act(act, L.plan, st);
     if (e != hipSuccess) return hip_fail(e, name);
 
     twq::DualArgs a{};
@@ -172,6 +191,19 @@ twq_status linear_impl(const void *x, const void *qw, const float *sw, const voi
     return e == hipSuccess ? TWQ_OK : hip_fail(e, name);
 }
 
+int hip_error(hipError_t e, const char *where) { return hip_fail(e, where); }
+
+}  // namespace twq
+
+namespace {
+
+twq_status linear_impl(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t, int64_t r,
+                       void *y, int64_t b, int64_t m, int64_t n, int group, void *workspace, size_t workspace_bytes,
+                       void *stream, const char *name, int a8 = 0, bool main_only = false) {
+    return (twq_status)twq::linear_run(x, qw, sw, l1t, l2t, r, y, b, m, n, group, workspace, workspace_bytes, stream,
+                                       name, a8, main_only);
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,6 +222,8 @@ const char *twq_status_string(int status) {
 }
 
 const char *twq_last_error_string(void) { return g_last_error; }
+
+const char *twq_last_hip_error(void) { return g_last_error; }
 
 int twq_version(void) { return 100; }
 
@@ -329,6 +363,13 @@ twq_status twq_linear(const void *x, const void *qw, const float *sw, const void
     return linear_impl(x, qw, sw, l1t, l2t, r, y, b, m, n, 0, workspace, workspace_bytes, stream, "twq_linear");
 }
 
+twq_status twq_debug_linear_main(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t,
+                                 int64_t r, void *y, int64_t b, int64_t m, int64_t n, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    return linear_impl(x, qw, sw, l1t, l2t, r, y, b, m, n, 0, workspace, workspace_bytes, stream,
+                       "twq_debug_linear_main", 0, true);
+}
+
 size_t twq_linear_grouped_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r, int64_t g) {
     if (!valid_group(g) || !valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return 0;
     return linear_layout(b, m, n, r, (int)g).total;
@@ -340,6 +381,14 @@ twq_status twq_linear_grouped(const void *x, const void *qw, const float *sw, co
     if (!valid_group(g)) return TWQ_ERR_UNSUPPORTED;
     return linear_impl(x, qw, sw, l1t, l2t, r, y, b, m, n, (int)g, workspace, workspace_bytes, stream,
                        "twq_linear_grouped");
+}
+
+twq_status twq_debug_linear_grouped_main(const void *x, const void *qw, const float *sw, const void *l1t,
+                                         const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n,
+                                         int64_t g, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!valid_group(g)) return TWQ_ERR_UNSUPPORTED;
+    return linear_impl(x, qw, sw, l1t, l2t, r, y, b, m, n, (int)g, workspace, workspace_bytes, stream,
+                       "twq_debug_linear_grouped_main", 0, true);
 }
 
 twq_status twq_quantize_act_a8(const void *x, int64_t b, int64_t m, void *qx, float *sx, const void *l1t, int64_t r,
@@ -361,6 +410,13 @@ twq_status twq_linear_a8(const void *x, const void *qw, const float *sw, const v
                          void *y, int64_t b, int64_t m, int64_t n, void *workspace, size_t workspace_bytes,
                          void *stream) {
     return linear_impl(x, qw, sw, l1t, l2t, r, y, b, m, n, 0, workspace, workspace_bytes, stream, "twq_linear_a8", 1);
+}
+
+twq_status twq_debug_linear_a8_main(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t,
+                                    int64_t r, void *y, int64_t b, int64_t m, int64_t n, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    return linear_impl(x, qw, sw, l1t, l2t, r, y, b, m, n, 0, workspace, workspace_bytes, stream,
+                       "twq_debug_linear_a8_main", 1, true);
 }
 
 twq_status twq_debug_residual_acc_a8(const void *qx, const void *qw, int32_t *acc, int64_t b, int64_t m, int64_t n,

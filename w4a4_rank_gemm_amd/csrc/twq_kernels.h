@@ -97,6 +97,21 @@ int dual_max_t_slices(int64_t b, int64_t m, int64_t n, int r);
 
 // ---- int4 low-rank variant ------------------------------------------------------------
 
+// ---- the one-call layer (twq_api.cpp), shared with the allocation-free entry point ----
+
+// Argument checks of twq_linear other than the workspace (a twq_status value).
+int linear_check(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t, int64_t r,
+                 const void *y, int64_t b, int64_t m, int64_t n);
+// Workspace bytes of the one-call layer (0 for invalid shapes).
+size_t linear_workspace(int64_t b, int64_t m, int64_t n, int64_t r, int group, int a8);
+// The body of twq_linear / _grouped / _a8 (a twq_status value); main_only: the fused
+// launch alone, on what an earlier call of the same shape left in the workspace.
+int linear_run(const void *x, const void *qw, const float *sw, const void *l1t, const void *l2t, int64_t r, void *y,
+               int64_t b, int64_t m, int64_t n, int group, void *workspace, size_t workspace_bytes, void *stream,
+               const char *name, int a8, bool main_only);
+// Records the HIP error text for twq_last_error_string; returns TWQ_ERR_HIP.
+int hip_error(hipError_t e, const char *where);
+
 hipError_t launch_pack_lowrank(const uint16_t *l1t, const uint16_t *l2t, int r, int64_t m, int64_t n, uint8_t *ql1,
                                float *sl1, uint8_t *ql2, float *sl2, float *c, hipStream_t stream);
 hipError_t launch_lowrank_requant(const uint8_t *qx, const float *sx, const uint8_t *ql1, const float *c, int r,
