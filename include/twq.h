@@ -162,6 +162,34 @@ twq_status twq_linear(const void *x, const void *qw, const float *sw, const void
                       size_t workspace_bytes, void *stream);
 
 /*
+ * twq_linear for callers that cannot allocate memory: code under HIP graph (stream)
+ * capture, serving loops and harnesses that forbid hipMalloc. It computes exactly
+ * what twq_linear computes (the same kernels; Y bitwise equal), but takes its scratch
+ * memory -- Q_X, s_X and T or T's partial sums between the two launches -- from a
+ * device array inside the library instead of a workspace argument, and calls no
+ * allocating routine.
+ *
+ *  - The array holds twq_linear_noalloc_max_bytes() bytes (64 MiB) on each GPU the
+ *    library runs this entry point on, from the first call there until the process
+ *    ends. A call whose scratch would exceed it (twq_linear_workspace_bytes(b, m, n,
+ *    r) > twq_linear_noalloc_max_bytes()) returns TWQ_ERR_WORKSPACE before any HIP
+ *    call.
+ *  - The array of the calling thread's current device (hipGetDevice) is used; the
+ *    stream must belong to that device.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *    contents; no initial contents are needed. Calls that may overlap in time on one
+ *    GPU (other streams, other threads) race on it and must be serialized by the
+ *    caller; calls on one stream never overlap.
+ *  - The first call on a device looks up the array's device address (not an
+ *    allocation); a failure there returns TWQ_ERR_HIP.
+ * Other arguments, checks and errors are those of twq_linear.
+ */
+size_t twq_linear_noalloc_max_bytes(void);
+twq_status twq_linear_noalloc(const void *x, const void *qw, const float *sw, const void *l1t,
+                              const void *l2t, int64_t r, void *y, int64_t b, int64_t m, int64_t n,
+                              void *stream);
+
+/*
  * Measurement export: the second launch of twq_linear alone -- the fused main loop
  * and epilogue, with exactly the kernel, grid and arguments twq_linear uses for this
  * shape -- reading Q_X, s_X and T (or T's partial sums over K slices) from a

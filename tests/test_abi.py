@@ -180,3 +180,22 @@ def test_panel_layout_helpers_follow_the_documented_offsets():
     assert np.array_equal(to_panels(rows).reshape(-1), flat)
     assert np.array_equal(from_panels(to_panels(rows)), rows)
 
+
+def test_linear_noalloc_limits_and_checks():
+    """twq_linear_noalloc: the same argument checks as twq_linear, and a size above its
+    fixed scratch array is refused before any HIP call."""
+    L = twq.lib()
+    cap = L.twq_linear_noalloc_max_bytes()
+    assert cap == 64 << 20
+    assert L.twq_linear_noalloc(A, A, A, A, A, 32, A, 16, 100, 4096, None) == SHAPE
+    assert L.twq_linear_noalloc(None, A, A, A, A, 32, A, 16, 4096, 4096, None) == NULL
+    assert L.twq_linear_noalloc(A, A, A, None, A, 32, A, 16, 4096, 4096, None) == NULL
+    assert L.twq_linear_noalloc(A, MIS, A, A, A, 32, A, 16, 4096, 4096, None) == ALIGN
+    assert L.twq_linear_noalloc(A, A, A, A, A, 32, A, 0, 4096, 4096, None) == OK  # empty call
+    # the largest token count whose scratch fits, and the next that does not
+    m, n, r = 8192, 28672, 128
+    fits = [b for b in (32, 1024, 4096, 8192, 16384, 65536)
+            if L.twq_linear_workspace_bytes(b, m, n, r) <= cap]
+    big = [b for b in (32, 1024, 4096, 8192, 16384, 65536) if b not in fits]
+    assert 8192 in fits and big, (fits, big)
+    assert L.twq_linear_noalloc(A, A, A, A, A, r, A, big[0], m, n, None) == WORKSPACE

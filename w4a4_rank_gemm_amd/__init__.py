@@ -33,7 +33,8 @@ EXPORTS = ("twq_status_string", "twq_last_error_string", "twq_last_hip_error", "
            "twq_dual_linear_a8", "twq_linear_a8_workspace_bytes", "twq_linear_a8", "twq_debug_residual_acc_a8",
            "twq_pack_lowrank_int4",
            "twq_lowrank_requant", "twq_dual_linear_lr4", "twq_debug_linear_main",
-           "twq_debug_linear_grouped_main", "twq_debug_linear_a8_main")
+           "twq_debug_linear_grouped_main", "twq_debug_linear_a8_main", "twq_linear_noalloc_max_bytes",
+           "twq_linear_noalloc")
 
 GROUP = 128  # group size of the group-wise entry points
 
@@ -112,6 +113,10 @@ def lib() -> ctypes.CDLL:
                 for nm in ("twq_debug_linear_main", "twq_debug_linear_a8_main"):
                     getattr(L, nm).restype = ctypes.c_int
                     getattr(L, nm).argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _S, _P]
+                L.twq_linear_noalloc_max_bytes.restype = _S
+                L.twq_linear_noalloc_max_bytes.argtypes = []
+                L.twq_linear_noalloc.restype = ctypes.c_int
+                L.twq_linear_noalloc.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P]
                 L.twq_debug_linear_grouped_main.restype = ctypes.c_int
                 L.twq_debug_linear_grouped_main.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _P, _S, _P]
                 _lib = L
@@ -257,6 +262,39 @@ def linear(x: torch.Tensor, qw, sw, l1t=None, l2t=None, out: torch.Tensor | None
     ws, wsb = _workspace(dev, L.twq_linear_workspace_bytes(b, m, n, r))
     _check(L.twq_linear(_ptr(x), _ptr(qw), _ptr(sw), _ptr(l1t), _ptr(l2t), r, _ptr(y), b, m, n,
                         _ptr(ws), wsb, _stream(dev)), "twq_linear")
+    return y
+
+
+def linear_noalloc(x: torch.Tensor, qw, sw, l1t=None, l2t=None, out: torch.Tensor | None = None):
+    """twq_linear_noalloc: the one-call layer on the library's own per-GPU scratch array
+    (no workspace, no allocation inside the call). Only `out`, if not given, is allocated
+    here, before the call; pass `out` to allocate nothing. Calls that may overlap on one
+    GPU share the scratch and must be serialized by the caller."""
+    _need(x, "x", torch.float16, 2)
+    _need(qw, "qw", torch.uint8, 2)
+    _need(sw, "sw", torch.float32, 1)
+    b, m = x.shape
+    n = qw.shape[0]
+    if qw.shape[1] != m // 2 or sw.shape[0] != n:
+        raise ValueError("inconsistent shapes of x/qw/sw")
+    r = 0
+    if l1t is not None or l2t is not None:
+        _need(l1t, "l1t", torch.float16, 2)
+        _need(l2t, "l2t", torch.float16, 2)
+        r = l1t.shape[0]
+        if l1t.shape[1] != m or l2t.shape != (n, r):
+            raise ValueError("l1t must be [r][m] and l2t [n][r]")
+    dev = x.device
+    for name, ten in (("qw", qw), ("sw", sw), ("l1t", l1t), ("l2t", l2t)):
+        if ten is not None and ten.device != dev:
+            raise ValueError(f"{name} is on {ten.device}, x on {dev}")
+    y = out if out is not None else torch.empty((b, n), dtype=torch.float16, device=dev)
+    _need(y, "out", torch.float16, 2)
+    if y.shape != (b, n):
+        raise ValueError("out must be [b][n]")
+    with torch.cuda.device(dev):
+        _check(lib().twq_linear_noalloc(_ptr(x), _ptr(qw), _ptr(sw), _ptr(l1t), _ptr(l2t), r, _ptr(y), b, m, n,
+                                        _stream(dev)), "twq_linear_noalloc")
     return y
 
 
