@@ -383,8 +383,8 @@ def main():
     ap.add_argument("--path", choices=("linear", "split"), default="linear",
                     help="linear: one twq_linear call per step; split: twq_quantize_act + twq_dual_linear")
     ap.add_argument("--lowrank", choices=("fp16", "int4"), default="fp16",
-                    help="fp16: the fp16 low-rank branch; int4: twq_quantize_act + twq_lowrank_requant "
-                         "+ twq_dual_linear_lr4 with 4-bit L1, L2 and H")
+                    help="fp16: the fp16 low-rank branch; int4: 4-bit L1, L2 and H (twq_linear_lr4, or "
+                         "twq_quantize_act_lr4 + twq_dual_linear_lr4 with --path split)")
     ap.add_argument("--group", type=int, choices=(0, 128), default=0,
                     help="128: group-wise scales (twq_*_grouped entry points, groups of 128 along K)")
     ap.add_argument("--act-bits", type=int, choices=(4, 8), default=4,
@@ -422,8 +422,6 @@ def main():
 
     lr4 = args.lowrank == "int4"
     grp = args.group
-    if lr4 and args.path != "linear":
-        ap.error("--lowrank int4 has one call sequence; leave --path at its default")
     a8 = args.act_bits == 8
     if lr4 and grp:
         ap.error("--group applies to the fp16 low-rank branch only")
@@ -452,19 +450,23 @@ def main():
         if lr4:
             s_.update({"ql1": lp0["ql1"].clone() if r else None, "c": lp0["c"].clone() if r else None,
                        "ql2": lp0["ql2"].clone() if r else None,
-                       "h": torch.empty((b, r), dtype=torch.int32, device=dev) if r else None,
                        "qh": torch.empty((b, r // 2), dtype=torch.uint8, device=dev) if r else None,
                        "sh": torch.empty((b,), dtype=torch.float32, device=dev) if r else None})
         sets.append(s_)
     del lp0
     L = twq.lib()
     ws, wsb = twq._workspace(dev, max(L.twq_quantize_act_workspace_bytes(b, m, r),
-                                      L.twq_linear_grouped_workspace_bytes(b, m, n, r, grp) if grp
+                                      L.twq_linear_lr4_workspace_bytes(b, m, n, r) if lr4
+                                      else L.twq_linear_grouped_workspace_bytes(b, m, n, r, grp) if grp
                                       else L.twq_linear_a8_workspace_bytes(b, m, n, r) if a8
                                       else L.twq_linear_workspace_bytes(b, m, n, r)))
     P = lambda t: None if t is None else twq.ctypes.c_void_p(t.data_ptr())
 
     def layer(s, stream):
+        if lr4:
+            twq._check(L.twq_linear_lr4(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["ql1"]), P(s["c"]), P(s["ql2"]), r,
+                                        P(s["y"]), b, m, n, P(ws), wsb, stream), "twq_linear_lr4")
+            return
         if a8:
             twq._check(L.twq_linear_a8(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["l1t"]), P(s["l2t"]), r, P(s["y"]),
                                        b, m, n, P(ws), wsb, stream), "twq_linear_a8")
@@ -485,11 +487,12 @@ def main():
             twq._check(L.twq_quantize_act_grouped(P(s["x"]), b, m, grp, P(s["qx"]), P(s["sx"]), P(s["l1t"]), r,
                                                   P(s["t"]), P(ws), wsb, stream), "twq_quantize_act_grouped")
             return
-        twq._check(L.twq_quantize_act(P(s["x"]), b, m, P(s["qx"]), P(s["sx"]), P(s["l1t"]), 0 if lr4 else r,
+        if lr4:
+            twq._check(L.twq_quantize_act_lr4(P(s["x"]), b, m, P(s["ql1"]), P(s["c"]), r, P(s["qx"]), P(s["sx"]),
+                                              P(s["qh"]), P(s["sh"]), stream), "twq_quantize_act_lr4")
+            return
+        twq._check(L.twq_quantize_act(P(s["x"]), b, m, P(s["qx"]), P(s["sx"]), P(s["l1t"]), r,
                                       P(s["t"]), P(ws), wsb, stream), "twq_quantize_act")
-        if lr4 and r:
-            twq._check(L.twq_lowrank_requant(P(s["qx"]), P(s["sx"]), P(s["ql1"]), P(s["c"]), r, P(s["h"]),
-                                             P(s["qh"]), P(s["sh"]), b, m, stream), "twq_lowrank_requant")
 
     def dual(s, stream):
         if a8:
@@ -525,7 +528,11 @@ def main():
     def layer_main(s, stream):
         # the fused launch of the one-call layer alone, on the Q_X, s_X and T (or T's
         # partial sums) that an earlier call of the same shape left in the workspace
-        if a8:
+        if lr4:
+            twq._check(L.twq_debug_linear_lr4_main(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["ql1"]), P(s["c"]),
+                                                   P(s["ql2"]), r, P(s["y"]), b, m, n, P(ws), wsb, stream),
+                       "twq_debug_linear_lr4_main")
+        elif a8:
             twq._check(L.twq_debug_linear_a8_main(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["l1t"]), P(s["l2t"]), r,
                                                   P(s["y"]), b, m, n, P(ws), wsb, stream), "twq_debug_linear_a8_main")
         elif grp:
@@ -536,7 +543,7 @@ def main():
             twq._check(L.twq_debug_linear_main(P(s["x"]), P(s["qw"]), P(s["sw"]), P(s["l1t"]), P(s["l2t"]), r,
                                                P(s["y"]), b, m, n, P(ws), wsb, stream), "twq_debug_linear_main")
 
-    one_call = args.path == "linear" and not lr4
+    one_call = args.path == "linear"
 
     def steps_fn(k, with_quant=True, offset=0):
         # with_quant=False: the main-loop kernel alone, exactly as the timed step
@@ -617,15 +624,14 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                 "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": traffic}
     sfx = "_grouped" if grp else "_a8" if a8 else ""
-    roof["kernel"] = ("twq_dual_linear_lr4" if lr4 else f"fused launch of twq_linear{sfx}" if one_call
-                      else f"twq_dual_linear{sfx}")
+    if lr4:
+        sfx = "_lr4"
+    roof["kernel"] = f"fused launch of twq_linear{sfx}" if one_call else f"twq_dual_linear{sfx}"
     roof["kernel_us"] = round(us_dual, 3)
     roof["algorithmic_bytes"] = kbytes
     roof["algorithmic_int8_ops"] = 2 * b * m * n
 
-    if lr4:
-        entry_points = "twq_quantize_act+twq_lowrank_requant+twq_dual_linear_lr4"
-    elif args.path == "linear":
+    if args.path == "linear":
         entry_points = f"twq_linear{sfx}"
     else:
         entry_points = f"twq_quantize_act{sfx}+twq_dual_linear{sfx}"

@@ -98,6 +98,8 @@ int twq_version(void);
  *                                      initial contents are needed. Calls that
  *                                      share a workspace must not overlap in time.
  */
+/* (The size covers each of twq_quantize_act, twq_quantize_act_grouped and
+ * twq_quantize_act_a8 for the same b, m, r.) */
 size_t twq_quantize_act_workspace_bytes(int64_t b, int64_t m, int64_t r);
 twq_status twq_quantize_act(const void *x, int64_t b, int64_t m, void *qx, float *sx,
                             const void *l1t, int64_t r, float *t, void *workspace,
@@ -300,24 +302,58 @@ twq_status twq_pack_lowrank_int4(const void *l1t, const void *l2t, int64_t r, in
                                  void *ql1, float *sl1, void *ql2, float *sl2, float *c, void *stream);
 
 /*
- * H = Q_X Q_L1^T and its requantization, once per call.
- *   qx, sx     from twq_quantize_act;  ql1, c  from twq_pack_lowrank_int4
- *   h     i32 [b][r]    (out)          the exact integer H
- *   qh    u8  [b][r/2]  (out)          packed Q_H
+ * The activation side of the int4 low-rank branch: per-token quantization of X (as
+ * twq_quantize_act, one launch), then H = Q_X Q_L1^T (exact, int32 on int8 matrix
+ * cores) requantized on chip as described above, by CTAs that each hold every rank of
+ * their tokens (TwinQuant page 1, section 4.3: the low-rank intermediate is
+ * requantized on the fly and never written to global memory). Only Q_H and s_H are
+ * stored.
+ *   x     fp16 [b][m];  ql1, c  from twq_pack_lowrank_int4;  r a multiple of 32, 32..256
+ *   qx    u8  [b][m/2]  (out)          packed Q_X
+ *   sx    f32 [b]       (out)          s_X per token
+ *   qh    u8  [b][r/2]  (out)          packed Q_H (K = r contiguous per token)
  *   sh    f32 [b]       (out)          s_H per token
  */
-twq_status twq_lowrank_requant(const void *qx, const float *sx, const void *ql1, const float *c,
-                               int64_t r, int32_t *h, void *qh, float *sh, int64_t b, int64_t m,
-                               void *stream);
+twq_status twq_quantize_act_lr4(const void *x, int64_t b, int64_t m, const void *ql1, const float *c,
+                                int64_t r, void *qx, float *sx, void *qh, float *sh, void *stream);
 
 /*
- * The fused layer with the int4 low-rank branch (see above); qh, sh from
- * twq_lowrank_requant, ql2 from twq_pack_lowrank_int4; qh, sh, ql2 may be NULL
- * when r == 0.
+ * Test export: twq_quantize_act_lr4 (the same kernels, one template argument apart)
+ * that also stores the exact integer H [b][r] (int32) it requantizes, so the
+ * integer path can be checked bit for bit. The product path never stores H.
+ */
+twq_status twq_debug_lr4_h(const void *x, int64_t b, int64_t m, const void *ql1, const float *c,
+                           int64_t r, int32_t *h, void *qx, float *sx, void *qh, float *sh,
+                           void *stream);
+
+/*
+ * The fused layer with the int4 low-rank branch (see above); qx, sx, qh, sh from
+ * twq_quantize_act_lr4, ql2 from twq_pack_lowrank_int4; qh, sh, ql2 may be NULL when
+ * r == 0.
  */
 twq_status twq_dual_linear_lr4(const void *qx, const float *sx, const void *qw, const float *sw,
                                const void *qh, const float *sh, const void *ql2, int64_t r,
                                void *y, int64_t b, int64_t m, int64_t n, void *stream);
+
+/*
+ * The whole layer with the int4 low-rank branch in one call: twq_quantize_act_lr4 then
+ * twq_dual_linear_lr4 (three launches), with Q_X, s_X, Q_H and s_H kept in the workspace.
+ * Y is bitwise the result of those two calls.
+ *   x fp16 [b][m]; qw, sw from twq_pack_weight; ql1, c, ql2 from twq_pack_lowrank_int4;
+ *   r a multiple of 32, 32..256; y fp16 [b][n] (out)
+ *   workspace, workspace_bytes         at least twq_linear_lr4_workspace_bytes(b, m, n, r)
+ *                                      bytes; no initial contents are needed. Calls that
+ *                                      share a workspace must not overlap in time.
+ */
+size_t twq_linear_lr4_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r);
+twq_status twq_linear_lr4(const void *x, const void *qw, const float *sw, const void *ql1,
+                          const float *c, const void *ql2, int64_t r, void *y, int64_t b, int64_t m,
+                          int64_t n, void *workspace, size_t workspace_bytes, void *stream);
+/* Measurement export: the second launch of twq_linear_lr4 alone (as twq_debug_linear_main). */
+twq_status twq_debug_linear_lr4_main(const void *x, const void *qw, const float *sw, const void *ql1,
+                                     const float *c, const void *ql2, int64_t r, void *y, int64_t b,
+                                     int64_t m, int64_t n, void *workspace, size_t workspace_bytes,
+                                     void *stream);
 
 #ifdef __cplusplus
 }

@@ -63,7 +63,9 @@ def test_quantize_act_workspace():
     assert L.twq_quantize_act_workspace_bytes(16, 4096, 0) == 0
     assert L.twq_quantize_act_workspace_bytes(16, 100, 32) == 0  # invalid shape
     assert L.twq_quantize_act(A, 2048, 4096, A, A, A, 32, A, None, 0, None) == WORKSPACE
-    assert L.twq_quantize_act(A, 2048, 4096, A, A, A, 32, A, A, need - 1, None) == WORKSPACE
+    assert L.twq_quantize_act_a8(A, 2048, 4096, A, A, A, 32, A, None, 0, None) == WORKSPACE
+    assert L.twq_quantize_act_grouped(A, 2048, 4096, 128, A, A, A, 32, A, A, need - 1, None) == WORKSPACE
+    assert L.twq_quantize_act(A, 16, 4096, A, A, A, 32, A, None, 0, None) == WORKSPACE  # few tokens
 
 
 def test_empty_calls_are_no_ops():
@@ -102,15 +104,27 @@ def test_lowrank_int4_validation():
     L = twq.lib()
     # ranks must be a multiple of 32 for the int4 low-rank variant
     assert L.twq_pack_lowrank_int4(A, A, 16, 256, 32, A, A, A, A, A, None) == SHAPE
-    assert L.twq_lowrank_requant(A, A, A, A, 48, A, A, A, 4, 256, None) == SHAPE
+    assert L.twq_quantize_act_lr4(A, 4, 256, A, A, 48, A, A, A, A, None) == SHAPE
+    assert L.twq_quantize_act_lr4(A, 4, 256, A, A, 0, A, A, A, A, None) == SHAPE
+    assert L.twq_quantize_act_lr4(A, 4, 256, A, A, 288, A, A, A, A, None) == SHAPE
+    assert L.twq_linear_lr4(A, A, A, A, A, A, 48, A, 4, 256, 32, A, 1 << 30, None) == SHAPE
     assert L.twq_dual_linear_lr4(A, A, A, A, A, A, A, 16, A, 4, 256, 32, None) == SHAPE
     assert L.twq_pack_lowrank_int4(None, A, 32, 256, 32, A, A, A, A, A, None) == NULL
-    assert L.twq_lowrank_requant(A, A, A, A, 32, None, A, A, 4, 256, None) == NULL
+    assert L.twq_quantize_act_lr4(A, 4, 256, None, A, 32, A, A, A, A, None) == NULL
+    assert L.twq_quantize_act_lr4(A, 4, 256, A, A, 32, A, A, None, A, None) == NULL
+    assert L.twq_debug_lr4_h(A, 4, 256, A, A, 32, None, A, A, A, A, None) == NULL
+    assert L.twq_quantize_act_lr4(A, 4, 256, A, MIS, 32, A, A, A, A, None) == ALIGN
+    assert L.twq_linear_lr4(A, A, A, A, A, None, 32, A, 4, 256, 32, A, 1 << 30, None) == NULL
+    need = L.twq_linear_lr4_workspace_bytes(4, 256, 32, 32)
+    assert need >= 4 * 128 + 4 * 4 + 4 * 16 + 4 * 4
+    assert L.twq_linear_lr4(A, A, A, A, A, A, 32, A, 4, 256, 32, A, need - 1, None) == WORKSPACE
+    assert L.twq_linear_lr4(A, A, A, A, A, A, 32, A, 4, 256, 32, None, need, None) == WORKSPACE
     assert L.twq_dual_linear_lr4(A, A, A, A, None, A, A, 32, A, 4, 256, 32, None) == NULL
     assert L.twq_dual_linear_lr4(A, A, A, A, A, A, MIS, 32, A, 4, 256, 32, None) == ALIGN
     # empty calls
     assert L.twq_pack_lowrank_int4(None, None, 0, 256, 32, None, None, None, None, None, None) == OK
-    assert L.twq_lowrank_requant(None, None, None, None, 32, None, None, None, 0, 256, None) == OK
+    assert L.twq_quantize_act_lr4(None, 0, 256, None, None, 32, None, None, None, None, None) == OK
+    assert L.twq_linear_lr4(None, None, None, None, None, None, 32, None, 0, 256, 32, None, 0, None) == OK
     assert L.twq_dual_linear_lr4(None, None, None, None, None, None, None, 32, None, 0, 256, 32, None) == OK
 
 

@@ -32,18 +32,25 @@ def _np(t):
 
 
 def run_lr4(d):
+    """The int4 low-rank layer on the GPU: the activation launch through the product entry
+    point and through the test export that also stores H (they must agree bit for bit),
+    the fused launch, and the one-call layer (bitwise equal to the two calls)."""
     assert torch.cuda.is_available(), "GPU tests need an MI355X"
     dev = torch.device("cuda:0")
     x = torch.from_numpy(d["x"]).to(dev)
     w = torch.from_numpy(d["w_res"]).to(dev)
     l1t = torch.from_numpy(d["l1t"]).to(dev)
     l2t = torch.from_numpy(d["l2t"]).to(dev)
-    qx, sx, _ = twq.quantize_act(x)
     qw, sw = twq.pack_weight(w)
     f = twq.pack_lowrank_int4(l1t, l2t)
-    h, qh, sh = twq.lowrank_requant(qx, sx, f["ql1"], f["c"])
+    qx, sx, qh, sh = twq.quantize_act_lr4(x, f)
+    qx_d, sx_d, qh_d, sh_d, h = twq.quantize_act_lr4(x, f, debug_h=True)
     y = twq.dual_linear_lr4(qx, sx, qw, sw, qh, sh, f["ql2"])
+    y1 = twq.linear_lr4(x, qw, sw, f)
     torch.cuda.synchronize()
+    for name, a_, b_ in (("qx", qx, qx_d), ("sx", sx, sx_d), ("qh", qh, qh_d), ("sh", sh, sh_d)):
+        assert torch.equal(a_, b_), f"{name}: product entry point and test export differ"
+    assert torch.equal(y, y1), "twq_linear_lr4 differs from twq_quantize_act_lr4 + twq_dual_linear_lr4"
     return {"qx": qx, "sx": sx, "f": f, "h": h, "qh": qh, "sh": sh, "y": y}
 
 
@@ -99,6 +106,8 @@ def test_lr4_full_compare(b, m, n, r):
     d = synth.make_random(b, m, n, r, seed=3 * b + r)
     g = run_lr4(d)
     check_factors(d, g)
+    _, qxp_ref, sx_ref = oracle.quantize_act(d["x"])
+    assert np.array_equal(_np(g["qx"]), qxp_ref) and np.array_equal(_np(g["sx"]), sx_ref), "Q_X, s_X"
     ref = oracle.dual_linear_lr4(d["x"], d["w_res"], d["l1t"], d["l2t"])
     assert np.array_equal(_np(g["h"]).astype(np.int64), ref["h"]), "H"
     assert np.array_equal(_np(g["qh"]), ref["qh_packed"]), "Q_H"
@@ -122,10 +131,11 @@ def test_lr4_rank0_is_plain_w4a4():
     assert torch.equal(y, y_plain)
 
 
-@pytest.mark.parametrize("name", ["70b_gate_up_decode", "70b_gate_up_prefill"])
+@pytest.mark.parametrize("name", ["70b_gate_up_decode", "70b_gate_up_prefill", "gate_up_prefill", "down_prefill"])
 def test_lr4_full_size_sampled(name):
-    """The 70B-size gate/up layer with the int4 low-rank branch, both token counts:
-    factors, H, Q_H and s_H compared whole, Y at 384 sampled positions."""
+    """Full-size layers with the int4 low-rank branch (the 70B-size gate/up layer at both
+    token counts, the 8B gate/up and down layers at prefill): factors, Q_X, s_X, H, Q_H
+    and s_H compared whole, Y at 384 sampled positions."""
     _say(f"lr4 {name}: generating inputs")
     d = synth.make_layer(name)
     b, m = d["x"].shape
@@ -133,7 +143,8 @@ def test_lr4_full_size_sampled(name):
     _say(f"lr4 {name}: GPU b={b} m={m} n={n} r={r}")
     g = run_lr4(d)
     ref_f = check_factors(d, g)
-    qx, _, sx = oracle.quantize_act(d["x"])
+    qx, qxp, sx = oracle.quantize_act(d["x"])
+    assert np.array_equal(_np(g["qx"]), qxp) and np.array_equal(_np(g["sx"]), sx), "Q_X, s_X"
     rq = oracle.lowrank_requant(qx, sx, ref_f["ql1"], ref_f["c"])
     assert np.array_equal(_np(g["h"]).astype(np.int64), rq["h"]), "H"
     assert np.array_equal(_np(g["qh"]), rq["qh_packed"]), "Q_H"

@@ -217,18 +217,21 @@ def test_workspace_shared_across_shapes():
 
 
 def test_workspace_too_small_is_rejected():
+    """The many-token quantizers keep T's K-slice partial sums in the workspace."""
     dev = _dev()
     L = twq.lib()
     b, m, r = 2048, 4096, 32
     x = torch.zeros(b, m, dtype=torch.float16, device=dev)
     l1t = torch.zeros(r, m, dtype=torch.float16, device=dev)
-    qx = torch.empty(b, m // 2, dtype=torch.uint8, device=dev)
+    qx = torch.empty(b, m, dtype=torch.uint8, device=dev)
     sx = torch.empty(b, dtype=torch.float32, device=dev)
     t = torch.empty(b, r, dtype=torch.float32, device=dev)
     need = L.twq_quantize_act_workspace_bytes(b, m, r)
+    assert need > 0
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     import ctypes
     p = lambda z: ctypes.c_void_p(z.data_ptr())
+    assert L.twq_quantize_act_a8(p(x), b, m, p(qx), p(sx), p(l1t), r, p(t), p(ws), need - 16, None) == 6
     assert L.twq_quantize_act(p(x), b, m, p(qx), p(sx), p(l1t), r, p(t), p(ws), need - 16, None) == 6
 
 

@@ -32,7 +32,8 @@ EXPORTS = ("twq_status_string", "twq_last_error_string", "twq_last_hip_error", "
            "twq_linear_grouped_workspace_bytes", "twq_linear_grouped", "twq_quantize_act_a8",
            "twq_dual_linear_a8", "twq_linear_a8_workspace_bytes", "twq_linear_a8", "twq_debug_residual_acc_a8",
            "twq_pack_lowrank_int4",
-           "twq_lowrank_requant", "twq_dual_linear_lr4", "twq_debug_linear_main",
+           "twq_quantize_act_lr4", "twq_debug_lr4_h", "twq_dual_linear_lr4", "twq_linear_lr4_workspace_bytes",
+           "twq_linear_lr4", "twq_debug_linear_lr4_main", "twq_debug_linear_main",
            "twq_debug_linear_grouped_main", "twq_debug_linear_a8_main", "twq_linear_noalloc_max_bytes",
            "twq_linear_noalloc")
 
@@ -106,8 +107,15 @@ def lib() -> ctypes.CDLL:
                 L.twq_debug_residual_acc_a8.argtypes = [_P, _P, _P, _I, _I, _I, _P]
                 L.twq_pack_lowrank_int4.restype = ctypes.c_int
                 L.twq_pack_lowrank_int4.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P]
-                L.twq_lowrank_requant.restype = ctypes.c_int
-                L.twq_lowrank_requant.argtypes = [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _P]
+                L.twq_quantize_act_lr4.restype = ctypes.c_int
+                L.twq_quantize_act_lr4.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P]
+                L.twq_debug_lr4_h.restype = ctypes.c_int
+                L.twq_debug_lr4_h.argtypes = [_P, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P]
+                L.twq_linear_lr4_workspace_bytes.restype = _S
+                L.twq_linear_lr4_workspace_bytes.argtypes = [_I, _I, _I, _I]
+                for nm in ("twq_linear_lr4", "twq_debug_linear_lr4_main"):
+                    getattr(L, nm).restype = ctypes.c_int
+                    getattr(L, nm).argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _S, _P]
                 L.twq_dual_linear_lr4.restype = ctypes.c_int
                 L.twq_dual_linear_lr4.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P]
                 for nm in ("twq_debug_linear_main", "twq_debug_linear_a8_main"):
@@ -513,21 +521,52 @@ def pack_lowrank_int4(l1t: torch.Tensor, l2t: torch.Tensor):
     return out
 
 
-def lowrank_requant(qx, sx, ql1, c):
-    """H = Q_X Q_L1^T (int32 [b][r]), Q_H u8 [b][r/2], s_H f32 [b]."""
-    _need(qx, "qx", torch.uint8, 2)
-    _need(sx, "sx", torch.float32, 1)
+def quantize_act_lr4(x: torch.Tensor, lp: dict, debug_h: bool = False):
+    """X fp16 [b][m] and the packed int4 factors (pack_lowrank_int4) -> (Q_X u8 [b][m/2],
+    s_X f32 [b], Q_H u8 [b][r/2], s_H f32 [b]); H = Q_X Q_L1^T is requantized on chip.
+    debug_h: through the test export twq_debug_lr4_h, which also returns the int32 H."""
+    _need(x, "x", torch.float16, 2)
+    ql1, c = lp["ql1"], lp["c"]
     _need(ql1, "ql1", torch.uint8, 2)
     _need(c, "c", torch.float32, 1)
-    b, kb = qx.shape
+    b, m = x.shape
     r = ql1.shape[0]
-    dev = qx.device
-    h = torch.empty((b, r), dtype=torch.int32, device=dev)
+    if ql1.shape[1] != m // 2 or c.shape[0] != r:
+        raise ValueError("ql1 must be [r][m/2] and c [r]")
+    dev = x.device
+    qx = torch.empty((b, m // 2), dtype=torch.uint8, device=dev)
+    sx = torch.empty((b,), dtype=torch.float32, device=dev)
     qh = torch.empty((b, r // 2), dtype=torch.uint8, device=dev)
     sh = torch.empty((b,), dtype=torch.float32, device=dev)
-    _check(lib().twq_lowrank_requant(_ptr(qx), _ptr(sx), _ptr(ql1), _ptr(c), r, _ptr(h), _ptr(qh), _ptr(sh),
-                                     b, 2 * kb, _stream(dev)), "twq_lowrank_requant")
-    return h, qh, sh
+    if debug_h:
+        h = torch.empty((b, r), dtype=torch.int32, device=dev)
+        _check(lib().twq_debug_lr4_h(_ptr(x), b, m, _ptr(ql1), _ptr(c), r, _ptr(h), _ptr(qx), _ptr(sx), _ptr(qh),
+                                     _ptr(sh), _stream(dev)), "twq_debug_lr4_h")
+        return qx, sx, qh, sh, h
+    _check(lib().twq_quantize_act_lr4(_ptr(x), b, m, _ptr(ql1), _ptr(c), r, _ptr(qx), _ptr(sx), _ptr(qh), _ptr(sh),
+                                      _stream(dev)), "twq_quantize_act_lr4")
+    return qx, sx, qh, sh
+
+
+def linear_lr4(x: torch.Tensor, qw, sw, lp: dict, out: torch.Tensor | None = None):
+    """The whole layer with the int4 low-rank branch in one call (twq_linear_lr4)."""
+    _need(x, "x", torch.float16, 2)
+    _need(qw, "qw", torch.uint8, 2)
+    _need(sw, "sw", torch.float32, 1)
+    b, m = x.shape
+    n = qw.shape[0]
+    ql1, c, ql2 = lp["ql1"], lp["c"], lp["ql2"]
+    r = ql1.shape[0]
+    if qw.shape[1] != m // 2 or sw.shape[0] != n or ql1.shape[1] != m // 2 or ql2.shape != (n, r // 2):
+        raise ValueError("inconsistent shapes of x/qw/sw/ql1/ql2")
+    dev = x.device
+    y = out if out is not None else torch.empty((b, n), dtype=torch.float16, device=dev)
+    _need(y, "out", torch.float16, 2)
+    L = lib()
+    ws, wsb = _workspace(dev, L.twq_linear_lr4_workspace_bytes(b, m, n, r))
+    _check(L.twq_linear_lr4(_ptr(x), _ptr(qw), _ptr(sw), _ptr(ql1), _ptr(c), _ptr(ql2), r, _ptr(y), b, m, n,
+                            _ptr(ws), wsb, _stream(dev)), "twq_linear_lr4")
+    return y
 
 
 def dual_linear_lr4(qx, sx, qw, sw, qh, sh, ql2, out: torch.Tensor | None = None):

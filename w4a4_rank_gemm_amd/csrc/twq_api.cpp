@@ -311,20 +311,6 @@ twq_status twq_pack_lowrank_int4(const void *l1t, const void *l2t, int64_t r, in
     return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_pack_lowrank_int4");
 }
 
-twq_status twq_lowrank_requant(const void *qx, const float *sx, const void *ql1, const float *c, int64_t r, int32_t *h,
-                               void *qh, float *sh, int64_t b, int64_t m, void *stream) {
-    if (!valid_b(b) || !valid_m(m) || !valid_r4(r)) return TWQ_ERR_SHAPE;
-    if (b == 0 || r == 0) return TWQ_OK;
-    if (!qx || !sx || !ql1 || !c || !h || !qh || !sh) return TWQ_ERR_NULL;
-    if (!aligned16(qx) || !aligned16(sx) || !aligned16(ql1) || !aligned16(c) || !aligned16(h) || !aligned16(qh) ||
-        !aligned16(sh))
-        return TWQ_ERR_ALIGN;
-    const hipError_t e = twq::launch_lowrank_requant(
-        static_cast<const uint8_t *>(qx), sx, static_cast<const uint8_t *>(ql1), c, (int)r, h,
-        static_cast<uint8_t *>(qh), sh, b, m, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_lowrank_requant");
-}
-
 twq_status twq_dual_linear_lr4(const void *qx, const float *sx, const void *qw, const float *sw, const void *qh,
                                const float *sh, const void *ql2, int64_t r, void *y, int64_t b, int64_t m, int64_t n,
                                void *stream) {
@@ -351,6 +337,118 @@ twq_status twq_dual_linear_lr4(const void *qx, const float *sx, const void *qw, 
     a.ql2 = static_cast<const uint8_t *>(ql2);
     const hipError_t e = twq::launch_dual_linear(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_dual_linear_lr4");
+}
+
+// ---- int4 low-rank branch: the activation launch with Q_H formed on chip ----
+
+namespace {
+
+struct Lr4Layout {
+    size_t qx, sx, qh, sh, total;
+};
+
+Lr4Layout lr4_layout(int64_t b, int64_t m, int64_t r) {
+    Lr4Layout L{};
+    L.qx = 0;
+    L.sx = align256((size_t)(b * m / 2));
+    L.qh = L.sx + align256((size_t)b * 4);
+    L.sh = L.qh + align256((size_t)(b * r / 2));
+    L.total = L.sh + align256((size_t)b * 4);
+    return L;
+}
+
+twq_status quantize_act_lr4_impl(const void *x, int64_t b, int64_t m, const void *ql1, const float *c, int64_t r,
+                                 void *qx, float *sx, void *qh, float *sh, int32_t *h, void *stream,
+                                 const char *name) {
+    if (!valid_b(b) || !valid_m(m) || !valid_r4(r) || r == 0) return TWQ_ERR_SHAPE;
+    if (b == 0) return TWQ_OK;
+    if (!x || !ql1 || !c || !qx || !sx || !qh || !sh) return TWQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(ql1) || !aligned16(c) || !aligned16(qx) || !aligned16(sx) || !aligned16(qh) ||
+        !aligned16(sh) || (h && !aligned16(h)))
+        return TWQ_ERR_ALIGN;
+    // the per-token quantizer (no first low-rank product: r = 0), then H and Q_H on chip
+    twq::ActArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.b = b;
+    a.m = m;
+    a.qx = static_cast<uint8_t *>(qx);
+    a.sx = sx;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = twq::launch_act(a, twq::plan_act(b, m, 0), st);
+    if (e == hipSuccess)
+        e = twq::launch_lowrank_requant(static_cast<const uint8_t *>(qx), sx, static_cast<const uint8_t *>(ql1), c,
+                                        (int)r, static_cast<uint8_t *>(qh), sh, h, b, m, st);
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, name);
+}
+
+twq_status linear_lr4_impl(const void *x, const void *qw, const float *sw, const void *ql1, const float *c,
+                           const void *ql2, int64_t r, void *y, int64_t b, int64_t m, int64_t n, void *workspace,
+                           size_t workspace_bytes, void *stream, const char *name, bool main_only) {
+    if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r4(r) || r == 0) return TWQ_ERR_SHAPE;
+    if (b == 0 || n == 0) return TWQ_OK;
+    if (!x || !qw || !sw || !ql1 || !c || !ql2 || !y) return TWQ_ERR_NULL;
+    if (!aligned16(x) || !aligned16(qw) || !aligned16(sw) || !aligned16(ql1) || !aligned16(c) || !aligned16(ql2) ||
+        !aligned16(y))
+        return TWQ_ERR_ALIGN;
+    const Lr4Layout L = lr4_layout(b, m, r);
+    if (!workspace || workspace_bytes < L.total) return TWQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return TWQ_ERR_ALIGN;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    void *qx = ws + L.qx, *qh = ws + L.qh;
+    float *sx = reinterpret_cast<float *>(ws + L.sx), *sh = reinterpret_cast<float *>(ws + L.sh);
+    if (!main_only) {
+        const twq_status st = quantize_act_lr4_impl(x, b, m, ql1, c, r, qx, sx, qh, sh, nullptr, stream, name);
+        if (st != TWQ_OK) return st;
+    }
+    twq::DualArgs a{};
+    a.qx = static_cast<const uint8_t *>(qx);
+    a.sx = sx;
+    a.qw = static_cast<const uint8_t *>(qw);
+    a.sw = sw;
+    a.r = (int)r;
+    a.y = static_cast<uint16_t *>(y);
+    a.b = b;
+    a.m = m;
+    a.n = n;
+    a.lr4 = 1;
+    a.tks = 1;
+    a.qh = static_cast<const uint8_t *>(qh);
+    a.sh = sh;
+    a.ql2 = static_cast<const uint8_t *>(ql2);
+    const hipError_t e = twq::launch_dual_linear(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, name);
+}
+
+}  // namespace
+
+twq_status twq_quantize_act_lr4(const void *x, int64_t b, int64_t m, const void *ql1, const float *c, int64_t r,
+                                void *qx, float *sx, void *qh, float *sh, void *stream) {
+    return quantize_act_lr4_impl(x, b, m, ql1, c, r, qx, sx, qh, sh, nullptr, stream, "twq_quantize_act_lr4");
+}
+
+twq_status twq_debug_lr4_h(const void *x, int64_t b, int64_t m, const void *ql1, const float *c, int64_t r,
+                           int32_t *h, void *qx, float *sx, void *qh, float *sh, void *stream) {
+    if (!h && valid_b(b) && b > 0) return TWQ_ERR_NULL;
+    return quantize_act_lr4_impl(x, b, m, ql1, c, r, qx, sx, qh, sh, h, stream, "twq_debug_lr4_h");
+}
+
+size_t twq_linear_lr4_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r) {
+    if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r4(r)) return 0;
+    return lr4_layout(b, m, r).total;
+}
+
+twq_status twq_linear_lr4(const void *x, const void *qw, const float *sw, const void *ql1, const float *c,
+                          const void *ql2, int64_t r, void *y, int64_t b, int64_t m, int64_t n, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    return linear_lr4_impl(x, qw, sw, ql1, c, ql2, r, y, b, m, n, workspace, workspace_bytes, stream,
+                           "twq_linear_lr4", false);
+}
+
+twq_status twq_debug_linear_lr4_main(const void *x, const void *qw, const float *sw, const void *ql1, const float *c,
+                                     const void *ql2, int64_t r, void *y, int64_t b, int64_t m, int64_t n,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+    return linear_lr4_impl(x, qw, sw, ql1, c, ql2, r, y, b, m, n, workspace, workspace_bytes, stream,
+                           "twq_debug_linear_lr4_main", true);
 }
 
 size_t twq_linear_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r) {

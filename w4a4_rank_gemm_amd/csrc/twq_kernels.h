@@ -112,9 +112,13 @@ int linear_run(const void *x, const void *qw, const float *sw, const void *l1t, 
 // Records the HIP error text for twq_last_error_string; returns TWQ_ERR_HIP.
 int hip_error(hipError_t e, const char *where);
 
+// H = Q_X Q_L1^T and its requantization on chip (lowrank_int4.hip): qx packed [b][m/2],
+// sx [b], ql1 in the panel layout (r rows), c [r]; writes qh [b][r/2], sh [b] and, if h
+// is not NULL, the exact H [b][r] (int32) as well.
+hipError_t launch_lowrank_requant(const uint8_t *qx, const float *sx, const uint8_t *ql1, const float *c, int r,
+                                  uint8_t *qh, float *sh, int32_t *h, int64_t b, int64_t m, hipStream_t stream);
+
 hipError_t launch_pack_lowrank(const uint16_t *l1t, const uint16_t *l2t, int r, int64_t m, int64_t n, uint8_t *ql1,
                                float *sl1, uint8_t *ql2, float *sl2, float *c, hipStream_t stream);
-hipError_t launch_lowrank_requant(const uint8_t *qx, const float *sx, const uint8_t *ql1, const float *c, int r,
-                                  int32_t *h, uint8_t *qh, float *sh, int64_t b, int64_t m, hipStream_t stream);
 
 }  // namespace twq
