@@ -635,21 +635,24 @@ __device__ __forceinline__ void pf_finish(const DualArgs &a, v4f (&y)[FN][FM], i
                 }
         }
     }
-    // fp16 low-rank branch: y += L2^T (channels x ranks) . T^T (ranks x tokens)
+    // fp16 low-rank branch: y += L2^T (channels x ranks) . T^T (ranks x tokens). Rows are
+    // addressed by 32-bit element offsets from the uniform bases (n r and b r stay below
+    // 2^32 within the ABI's limits) rather than one 64-bit pointer per row.
+    const int64_t chb = ch0 + wn * (BN / WN) + li, tkb = tok0 + wm * (BM / WM) + li;
     for (int k0 = 0; k0 < (LR4 ? 0 : a.r); k0 += 32) {
         const int rank = k0 + g * 8;
         const bool live = rank < a.r;  // r is a multiple of 16: live means rank + 8 <= r
-        const int rk = live ? rank : 0;
+        const uint32_t rk = live ? rank : 0;
         v8h la[FN], tb[FM];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + li;
-            la[fn] = load_h8(a.l2t + (ch < a.n ? ch : a.n - 1) * a.r + rk);
+            const int64_t ch = chb + fn * 16;
+            la[fn] = load_h8(a.l2t + ((uint32_t)((ch < a.n ? ch : a.n - 1) * a.r) + rk));
         }
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
-            const float4 *tp = reinterpret_cast<const float4 *>(a.t + (tok < a.b ? tok : a.b - 1) * a.r + rk);
+            const int64_t tok = tkb + fm * 16;
+            const float4 *tp = reinterpret_cast<const float4 *>(a.t + ((uint32_t)((tok < a.b ? tok : a.b - 1) * a.r) + rk));
             tb[fm] = live ? f32x8_to_h8(tp[0], tp[1]) : v8h{};
         }
 #pragma unroll
@@ -758,14 +761,18 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     const int li = lane & 15, g = lane >> 4;
     const int wn = wave % WN, wm = wave / WN;
 
-    // block -> tile: contiguous per XCD, grouped GM token tiles at a time
-    const int64_t ntiles = (int64_t)tiles_n * tiles_m;
-    const int64_t o = xcd_order(blockIdx.x, ntiles);
-    const int64_t gsz = (int64_t)GM * tiles_n;
-    const int64_t grp = o / gsz, within = o % gsz;
-    const int64_t gm_here = (tiles_m - grp * GM) < GM ? (tiles_m - grp * GM) : GM;
-    const int64_t tm = grp * GM + within % gm_here, tn = within / gm_here;
-    const int64_t ch0 = tn * BN, tok0 = tm * BM;
+    // block -> tile: contiguous per XCD, grouped GM token tiles at a time. The tile count
+    // fits 32 bits (the launch grid does), and the tile indices are uniform: they are
+    // computed in 32-bit arithmetic and kept in scalar registers, which leaves the vector
+    // registers to the main loop.
+    const int ntiles = tiles_n * tiles_m;
+    const int o = (int)xcd_order(blockIdx.x, ntiles);
+    const int gsz = GM * tiles_n;
+    const int grp = o / gsz, within = o % gsz;
+    const int gm_here = (tiles_m - grp * GM) < GM ? (tiles_m - grp * GM) : GM;
+    const int tm = __builtin_amdgcn_readfirstlane(grp * GM + within % gm_here);
+    const int tn = __builtin_amdgcn_readfirstlane(within / gm_here);
+    const int64_t ch0 = (int64_t)tn * BN, tok0 = (int64_t)tm * BM;
     const int64_t kb = a.m / 2;
     const int nst = (int)(a.m / (2 * RB));  // m is a multiple of 2 RB
 
@@ -924,10 +931,17 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
         });
     }
 
+    // The epilogue's lane coordinates are recomputed from the thread index (one register
+    // across the main loop instead of four; the wave's are uniform): with four CTAs a
+    // compute unit, keeping all four live through the loop spilled them.
+    int te = tid;
+    asm volatile("" : "+v"(te));
+    const int li_e = te & 15, g_e = (te >> 4) & 3;
+    const int wn_e = wave_u % WN, wm_e = wave_u / WN;
     if constexpr (GRP)
-        pf_finish<BN, BM, WN, WM, false>(a, yg, ch0, tok0, wn, wm, li, g);
+        pf_finish<BN, BM, WN, WM, false>(a, yg, ch0, tok0, wn_e, wm_e, li_e, g_e);
     else
-        pf_epilogue<BN, BM, WN, WM, STORE_ACC, LR4, A8 ? 4 : 8>(a, acc, ch0, tok0, wn, wm, li, g);
+        pf_epilogue<BN, BM, WN, WM, STORE_ACC, LR4, A8 ? 4 : 8>(a, acc, ch0, tok0, wn_e, wm_e, li_e, g_e);
 }
 
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false,
