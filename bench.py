@@ -284,6 +284,24 @@ def _graph_time(fn, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps * 1e3
 
 
+def unfused_layer(twq, x, qx, sx, t, qw, sw, l1t, l2t, y, ws, wsb, stream):
+    """The unfused comparator of the fused layer (the pages' kernel-fusion baseline, page 2
+    section A.4): the same quantizer and residual kernel, but the residual result is
+    written to HBM as Y_res (twq_dual_linear with r = 0), then T L2 is a separate fp16
+    GEMM and Y_res + T L2 a separate add (platform library launches). Writes y in place.
+    All tensors on one GPU; qx, sx, t are scratch of the quantizer's output shapes."""
+    import torch
+    L = twq.lib()
+    P = lambda z: None if z is None else twq.ctypes.c_void_p(z.data_ptr())
+    b, m = x.shape
+    n = qw.shape[0]
+    r = 0 if l1t is None else l1t.shape[0]
+    twq._check(L.twq_quantize_act(P(x), b, m, P(qx), P(sx), P(l1t), r, P(t), P(ws), wsb, stream), "twq_quantize_act")
+    twq._check(L.twq_dual_linear(P(qx), P(sx), P(qw), P(sw), None, None, 0, P(y), b, m, n, stream), "twq_dual_linear")
+    if r:
+        y.add_(torch.nn.functional.linear(t.half(), l2t))
+
+
 COMPARE_CONFIGS = ("o_proj_decode", "70b_gate_up_decode", "gate_up_prefill", "70b_gate_up_prefill")
 SWEEP_RANKS = (0, 32, 64, 128, 256)
 
@@ -347,12 +365,8 @@ def compare(args):
 
         def unfused(i):
             s_ = sets[i % copies]
-            st = hs()
-            twq._check(L.twq_quantize_act(P(s_["x"]), b, m, P(s_["qx"]), P(s_["sx"]), P(s_["l1t"]), r, P(s_["t"]),
-                                          P(ws), wsb, st), "twq_quantize_act")
-            twq._check(L.twq_dual_linear(P(s_["qx"]), P(s_["sx"]), P(s_["qw"]), P(s_["sw"]), None, None, 0,
-                                         P(s_["y"]), b, m, n, st), "twq_dual_linear")
-            s_["y"].add_(torch.nn.functional.linear(s_["t"].half(), s_["l2t"]))
+            unfused_layer(twq, s_["x"], s_["qx"], s_["sx"], s_["t"], s_["qw"], s_["sw"], s_["l1t"], s_["l2t"], s_["y"],
+                          ws, wsb, hs())
 
         def fp16(i):
             sets[i % copies]["y"].copy_(torch.nn.functional.linear(sets[i % copies]["x"], w16[i % copies16]))

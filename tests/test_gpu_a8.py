@@ -14,6 +14,7 @@ import torch
 import oracle
 import synth
 import w4a4_rank_gemm_amd as twq
+from tests import layers
 from tests.test_gpu_parity import _random_shapes
 from tests.panels import to_panels
 
@@ -124,10 +125,11 @@ def test_a8_quantizer_ties():
     assert np.array_equal(_np(sx), s_ref) and np.array_equal(_np(qx), q_ref)
 
 
-@pytest.mark.parametrize("name", ["o_proj_decode", "gate_up_prefill", "70b_gate_up_decode"])
+@pytest.mark.parametrize("name", ["o_proj_decode", "gate_up_prefill", "70b_gate_up_decode", "down_prefill",
+                                  "70b_gate_up_prefill"])
 def test_a8_full_size_sampled(name):
     _say(f"a8 {name}: generating inputs")
-    d = synth.make_layer(name)
+    d = layers.layer(name)
     b, m = d["x"].shape
     n = d["w_res"].shape[0]
     _say(f"a8 {name}: GPU b={b} m={m} n={n} r={d['l1t'].shape[0]}")

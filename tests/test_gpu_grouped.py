@@ -14,6 +14,7 @@ import torch
 import oracle
 import synth
 import w4a4_rank_gemm_amd as twq
+from tests import layers
 from tests.test_gpu_parity import _random_shapes
 from tests.panels import to_panels
 from tests.test_gpu_quant_ties import _row
@@ -132,7 +133,7 @@ def test_grouped_repeat_bitwise():
     assert torch.equal(a["y"], b["y"]) and torch.equal(a["y1"], b["y1"])
 
 
-BIG = ["o_proj_decode", "gate_up_prefill", "70b_gate_up_decode"]
+BIG = ["o_proj_decode", "gate_up_prefill", "70b_gate_up_decode", "down_prefill", "70b_gate_up_prefill"]
 
 
 @pytest.mark.parametrize("name", BIG)
@@ -140,7 +141,7 @@ def test_grouped_full_size_sampled(name):
     """Full-size layer shapes: every code and group scale compared whole, Y at 384 sampled
     positions (plus the corners and the largest |Y|)."""
     _say(f"grouped {name}: generating inputs")
-    d = synth.make_layer(name)
+    d = layers.layer(name)
     b, m = d["x"].shape
     n = d["w_res"].shape[0]
     _say(f"grouped {name}: GPU b={b} m={m} n={n} r={d['l1t'].shape[0]}")

@@ -75,3 +75,30 @@ def test_linear_repeat_bitwise():
     l1t, l2t = torch.from_numpy(d["l1t"]).to(dev), torch.from_numpy(d["l2t"]).to(dev)
     ys = [twq.linear(x, qw, sw, l1t, l2t).cpu() for _ in range(3)]
     assert all(torch.equal(ys[0], y) for y in ys[1:])
+
+
+@pytest.mark.parametrize("name", ["70b_gate_up_decode", "70b_gate_up_prefill"])
+def test_linear_70b_full_size(name):
+    """twq_linear at both 70B-size gate/up shapes, as the benchmark runs it: Y bitwise
+    equal to twq_quantize_act + twq_dual_linear, and within 2e-3 * max|Y_or| of the oracle
+    at 384 sampled positions (plus the corners and the largest |Y|)."""
+    from tests import layers
+    _say(f"twq_linear {name}: generating inputs")
+    d = layers.layer(name)
+    b, m = d["x"].shape
+    n, r = d["w_res"].shape[0], d["l1t"].shape[0]
+    _say(f"twq_linear {name}: GPU b={b} m={m} n={n} r={r}")
+    y1, y2 = _run(d)
+    assert np.array_equal(y1, y2), "twq_linear differs from twq_quantize_act + twq_dual_linear"
+    rng = synth.rng_for(900 + b)
+    rows = rng.integers(0, b, 384)
+    cols = rng.integers(0, n, 384)
+    top = int(np.argmax(np.abs(y1.astype(np.float32))))
+    rows[:5] = [0, 0, b - 1, b - 1, top // n]
+    cols[:5] = [0, n - 1, 0, n - 1, top % n]
+    _, y_ref = oracle.dual_linear_sampled(d["x"], d["w_res"], d["l1t"], d["l2t"], rows, cols)
+    y = y1[rows, cols].astype(np.float64)
+    scale = np.abs(y_ref).max()
+    err = np.abs(y - y_ref).max()
+    assert err <= Y_TOL * scale, (err, scale)
+    _say(f"  sampled max|Y-Y_or| = {err:.3g}, max|Y_or| over samples = {scale:.3g}")

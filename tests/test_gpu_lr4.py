@@ -14,6 +14,7 @@ import torch
 import oracle
 import synth
 import w4a4_rank_gemm_amd as twq
+from tests import layers
 from tests.panels import from_panels, to_panels
 
 pytestmark = pytest.mark.gpu
@@ -137,7 +138,7 @@ def test_lr4_full_size_sampled(name):
     token counts, the 8B gate/up and down layers at prefill): factors, Q_X, s_X, H, Q_H
     and s_H compared whole, Y at 384 sampled positions."""
     _say(f"lr4 {name}: generating inputs")
-    d = synth.make_layer(name)
+    d = layers.layer(name)
     b, m = d["x"].shape
     n, r = d["w_res"].shape[0], d["l1t"].shape[0]
     _say(f"lr4 {name}: GPU b={b} m={m} n={n} r={r}")

@@ -15,6 +15,7 @@ import torch
 import oracle
 import synth
 import w4a4_rank_gemm_amd as twq
+from tests import layers
 from tests.panels import to_panels, from_panels
 
 pytestmark = pytest.mark.gpu
@@ -117,7 +118,7 @@ def test_e6_hand_worked_layer_padded():
 @pytest.mark.parametrize("name", ["tiny", "o_proj_decode"])
 def test_config_full(name):
     _say(f"config {name}")
-    d = synth.make_layer(name)
+    d = layers.layer(name)
     err, scale = check_full(d, run_gpu(d))
     _say(f"  max|Y-Y_or| = {err:.3g}, max|Y_or| = {scale:.3g}")
 
@@ -245,7 +246,7 @@ def test_config_full_size_sampled(name):
     """Full-size shapes in the launch configuration the benchmark uses: every code and
     scale compared whole, the accumulator and Y at 384 sampled positions."""
     _say(f"config {name}: generating inputs")
-    d = synth.make_layer(name)
+    d = layers.layer(name)
     b, m = d["x"].shape
     n = d["w_res"].shape[0]
     _say(f"config {name}: GPU b={b} m={m} n={n} r={d['l1t'].shape[0]}")
