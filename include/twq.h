@@ -355,6 +355,43 @@ twq_status twq_debug_linear_lr4_main(const void *x, const void *qw, const float 
                                      int64_t m, int64_t n, void *workspace, size_t workspace_bytes,
                                      void *stream);
 
+/*
+ * ---- offline preparation: folding given transforms into the split (TwinQuant page 1,
+ * section 4.1) ----
+ *
+ * With the weight split W = U V + R (eq. (3)) and given an orthogonal Q (m x m, applied
+ * to the activations: the layer is then fed X Q) and an invertible G (r x r, on the rank
+ * space), the folded operands are
+ *
+ *   U' = Q^T U_r G,   V' = G^-1 V_r,   R' = Q^T W - U' V',
+ *
+ * with U_r = U sqrt(S) and V_r = sqrt(S) V^T from the top-r SVD of W, which the caller
+ * computes with any dense linear algebra library. U' and V' are rounded to fp16 (one
+ * correctly rounded conversion each); R' is formed in binary64 from those rounded
+ * factors, so the split is exact against what the layer is given, and rounded to fp32.
+ * All arithmetic (the scalings, the products, G^-1 by Gauss-Jordan elimination with
+ * partial pivoting) runs in binary64 on the GPU. A singular G gives non-finite outputs.
+ * Runs once per layer, offline.
+ *
+ *   w     f64 [n][m]   W^T (one row per output channel; W is the pages' m x n weight)
+ *   u     f64 [m][r]   the top r left singular vectors of W (columns)
+ *   s     f64 [r]      the top r singular values
+ *   vt    f64 [r][n]   the top r right singular vectors (rows)
+ *   q     f64 [m][m]   orthogonal, or NULL for the identity
+ *   g     f64 [r][r]   invertible, or NULL for the identity
+ *   l1t   fp16 [r][m]  (out) U'^T, the layer's L1 transposed
+ *   l2t   fp16 [n][r]  (out) V'^T, the layer's L2 transposed
+ *   w_res f32 [n][m]   (out) R'^T, the residual for twq_pack_weight
+ *   workspace          at least twq_fold_workspace_bytes(m, n, r) bytes of scratch
+ * Shapes: 0 <= r <= min(m, n, 256); m, n >= 1 (any multiple; the layer's own limits
+ * apply when the outputs are packed). u, s, vt, l1t, l2t may be NULL when r == 0.
+ */
+size_t twq_fold_workspace_bytes(int64_t m, int64_t n, int64_t r);
+twq_status twq_fold_lowrank(const double *w, const double *u, const double *s, const double *vt,
+                            const double *q, const double *g, int64_t m, int64_t n, int64_t r,
+                            void *l1t, void *l2t, float *w_res, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

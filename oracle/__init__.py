@@ -17,7 +17,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "twq_oracle.c")
-LIB_PATH = os.path.join(_HERE, "libtwq_oracle.so")
+# TWQ_ORACLE_LIB names another build of twq_oracle.c to load (the CPU sanitizer test
+# runs the oracle's pins against an AddressSanitizer/UBSan build this way)
+LIB_PATH = os.environ.get("TWQ_ORACLE_LIB") or os.path.join(_HERE, "libtwq_oracle.so")
 CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-std=c11",
           "-Wall", "-Wextra", "-shared", "-fPIC"]
 

@@ -213,3 +213,18 @@ def test_linear_noalloc_limits_and_checks():
     big = [b for b in (32, 1024, 4096, 8192, 16384, 65536) if b not in fits]
     assert 8192 in fits and big, (fits, big)
     assert L.twq_linear_noalloc(A, A, A, A, A, r, A, big[0], m, n, None) == WORKSPACE
+
+
+def test_fold_validation():
+    """twq_fold_lowrank rejects bad shapes, missing operands and short workspaces before
+    any HIP call (r == 0 needs no workspace)."""
+    L = twq.lib()
+    need = L.twq_fold_workspace_bytes(512, 384, 32)
+    assert need >= (512 * 32 * 2 + 32 * 384 + 3 * 32 * 32) * 8
+    assert L.twq_fold_workspace_bytes(512, 384, 0) == 0
+    assert L.twq_fold_workspace_bytes(512, 16, 32) == 0  # r > n
+    args = lambda r, ws, wsb, u=A: (A, u, A, A, A, A, 512, 384, r, A, A, A, ws, wsb, None)
+    assert L.twq_fold_lowrank(*args(32, A, need - 1)) == WORKSPACE
+    assert L.twq_fold_lowrank(*args(32, A, need, u=None)) == NULL
+    assert L.twq_fold_lowrank(*args(520, A, need)) == SHAPE
+    assert L.twq_fold_lowrank(*args(32, MIS, need)) == ALIGN

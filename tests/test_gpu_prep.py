@@ -80,3 +80,45 @@ def test_fold_split_identity_is_plain_split():
     torch.cuda.synchronize()
     back = w_res.double() + l2t.double() @ l1t.double()
     assert (back - torch.from_numpy(w).to(dev).double()).abs().max().item() <= 1e-6
+
+
+def _ulp16(a):
+    """Spacing of fp16 at |a| (the distance to the next fp16 away from zero)."""
+    a = np.abs(a.astype(np.float16))
+    return (np.nextafter(a, np.float16(np.inf)).astype(np.float64) - a.astype(np.float64))
+
+
+@pytest.mark.parametrize("n,m,r,with_q,with_g", [(384, 512, 32, True, True), (200, 128, 64, False, True),
+                                                  (96, 256, 16, True, False), (64, 64, 0, True, False),
+                                                  (300, 256, 256, True, True)])
+def test_fold_kernels_match_oracle_on_the_same_svd(n, m, r, with_q, with_g):
+    """twq_fold_lowrank given the very SVD factors the oracle uses (so no sign ambiguity):
+    the fp16 factors equal the oracle's up to one fp16 step (the binary64 products differ
+    only in summation order, which can move a value across a rounding boundary), R' is
+    exact against the factors it was given (R' + L1 L2 = Q^T W within the fp32 rounding
+    of R'), and G^-1 from the kernel's elimination satisfies G V' = V_r."""
+    w, q, g, _ = _case(n, m, max(r, 1), 970 + r)
+    q = q if with_q else None
+    g = (g if with_g else None) if r else None
+    wmn = w.astype(np.float64).T  # m x n
+    u, s, vt = np.linalg.svd(wmn, full_matrices=False)
+    dev = torch.device("cuda:0")
+    T = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float64)).to(dev)
+    l1t, l2t, w_res = prep.fold_lowrank(T(wmn.T), T(u[:, :r]) if r else None, T(s[:r]) if r else None,
+                                        T(vt[:r]) if r else None, T(q), T(g), r)
+    torch.cuda.synchronize()
+    ol1t, ol2t, ow_res = oracle.fold_split(w, r, q, g)
+    for got, want in ((l1t.cpu().numpy(), ol1t), (l2t.cpu().numpy(), ol2t)):
+        diff = np.abs(got.astype(np.float64) - want.astype(np.float64))
+        assert (diff <= _ulp16(want) * 1.0001).all(), diff.max()
+    # exactness of the split against its own factors
+    qm = np.eye(m) if q is None else q
+    rot = qm.T @ wmn
+    back = w_res.cpu().numpy().astype(np.float64).T + l1t.cpu().numpy().astype(np.float64).T @ \
+        l2t.cpu().numpy().astype(np.float64).T
+    assert np.abs(back - rot).max() <= 2.0 ** -23 * np.abs(rot).max() + 1e-12
+    if g is not None:  # G V' = V_r up to the fp16 rounding of V'
+        v_r = np.sqrt(s[:r])[:, None] * vt[:r]
+        gv = g @ l2t.cpu().numpy().astype(np.float64).T
+        bound = 2.0 ** -11 * (np.abs(g) @ np.abs(l2t.cpu().numpy().astype(np.float64).T)) + 1e-12
+        assert (np.abs(gv - v_r) <= bound * 1.0001).all()

@@ -35,7 +35,7 @@ EXPORTS = ("twq_status_string", "twq_last_error_string", "twq_last_hip_error", "
            "twq_quantize_act_lr4", "twq_debug_lr4_h", "twq_dual_linear_lr4", "twq_linear_lr4_workspace_bytes",
            "twq_linear_lr4", "twq_debug_linear_lr4_main", "twq_debug_linear_main",
            "twq_debug_linear_grouped_main", "twq_debug_linear_a8_main", "twq_linear_noalloc_max_bytes",
-           "twq_linear_noalloc")
+           "twq_linear_noalloc", "twq_fold_workspace_bytes", "twq_fold_lowrank")
 
 GROUP = 128  # group size of the group-wise entry points
 
@@ -121,6 +121,10 @@ def lib() -> ctypes.CDLL:
                 for nm in ("twq_debug_linear_main", "twq_debug_linear_a8_main"):
                     getattr(L, nm).restype = ctypes.c_int
                     getattr(L, nm).argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _S, _P]
+                L.twq_fold_workspace_bytes.restype = _S
+                L.twq_fold_workspace_bytes.argtypes = [_I, _I, _I]
+                L.twq_fold_lowrank.restype = ctypes.c_int
+                L.twq_fold_lowrank.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _S, _P]
                 L.twq_linear_noalloc_max_bytes.restype = _S
                 L.twq_linear_noalloc_max_bytes.argtypes = []
                 L.twq_linear_noalloc.restype = ctypes.c_int

@@ -347,53 +347,6 @@ __global__ __launch_bounds__(256) void t_reduce_kernel(const float *partials, in
     *reinterpret_cast<v4f *>(t + i4 * 4) = sum;
 }
 
-static int64_t pow2_floor(int64_t v) {
-    int64_t p = 1;
-    while (p * 2 <= v) p *= 2;
-    return p;
-}
-
-ActPlan plan_act(int64_t b, int64_t m, int64_t r) {
-    ActPlan pl{};
-    pl.ks = 1;
-    pl.nsl = 1;
-    if (b == 0) return pl;
-    if (b > 128) {
-        // many tokens: 128-row tiles x all ranks; K slices (steps of 32, at least 512
-        // long, at most 32 of them) until about 256 CTAs
-        pl.mode = 0;
-        pl.row_tile = 128;
-        pl.row_tiles = (int)((b + 127) / 128);
-        int64_t ks = 1;
-        if (r > 0)
-            while ((int64_t)pl.row_tiles * ks < 256 && ks < 32 && m / (ks * 2) >= 512 && m % (ks * 2 * 32) == 0)
-                ks *= 2;
-        pl.ks = (int)ks;
-    } else {
-        // few tokens: every token x one 16-rank tile x one K slice per CTA, slices of
-        // about 32 KB of X and L1 each (a compute unit streams only tens of GB/s, so
-        // the read is spread wide; smaller slices measured slower, their partial sums
-        // costing more than they spread); each short token row is quantized by nsl CTAs
-        pl.mode = 1;
-        pl.fm = (int)((b + 15) / 16);
-        pl.row_tile = pl.fm * 16;
-        pl.row_tiles = (int)(r / 16);
-        const int64_t bytes = m * (16 * pl.fm + 16) * 2;
-        int64_t ks = pow2_floor(bytes / 32768 > 0 ? bytes / 32768 : 1);
-        const int64_t max_ks = m / 128 < 32 ? m / 128 : 32;  // each wave keeps at least one step
-        while (ks > max_ks) ks /= 2;
-        pl.ks = r > 0 ? (int)ks : 1;
-        int64_t nsl = 1;
-        while (b * nsl < 128 && (m / 8) / (nsl * 2) >= 32) nsl *= 2;
-        pl.nsl = (int)nsl;
-    }
-    if (r > 0 && pl.ks > 1) {
-        const int64_t rows_pad = pl.mode == 0 ? (int64_t)pl.row_tiles * 128 : (int64_t)pl.fm * 16;
-        pl.workspace_bytes = (size_t)pl.ks * rows_pad * r * sizeof(float);
-    }
-    return pl;
-}
-
 template <int MODE, int NT>
 static void launch_one(const ActArgs &a, const ActDev &p, int64_t grid, hipStream_t stream) {
     hipLaunchKernelGGL((act_kernel<MODE, NT>), dim3((unsigned)grid), dim3(kActThreads), 0, stream, a, p);

@@ -68,9 +68,6 @@ __host__ __device__ __forceinline__ int64_t xcd_order(int64_t bid, int64_t ntile
 // unconditional -- rows past n or b are clamped to a valid row and their outputs never
 // stored -- so nothing serialises them, and the low-rank operands of the epilogue are
 // loaded first so their latency hides under the main loop.
-// Most partial sums of T (K slices x 32-rank steps) one lane of a decode epilogue
-// holds; a shape with more slices gets T reduced first.
-constexpr int kMaxTSlices = 16;
 
 // Group-wise scales (GRP, groups of kGroup = 128 along K): one 64-byte piece of a
 // packed row is one group, so each piece's integer sum is formed from zero and added to
@@ -976,26 +973,6 @@ static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
                 : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false>(a, stream);
 }
 
-// Decode tiles (FN x FM blocks of 16 channels x 16 tokens per CTA, FM = ceil(b / 16)):
-// the widest channel tile that still leaves at least 192 CTAs, at most 2 blocks for 16
-// tokens and 4 for 64; for 32 tokens 2 blocks, or 8 where the grid stays that wide and
-// K is long enough (m >= 8192) for each of the eight waves of such a CTA to stream at
-// least 8 pieces. Wider tiles read Q_X from L2 fewer times; fewer CTAs than that leave
-// compute units idle. Measured on MI355X (same-process sweeps of 6 tilings on each of
-// 37 few-token shapes, m and n from 4096 to 28672, weights cold): within 6% of the best
-// tiling on every shape. false: many tokens, the LDS-ring kernel.
-static bool decode_shape(int64_t b, int64_t m, int64_t n, int &fn, int &fm) {
-    if (b > 64) return false;
-    fm = b <= 16 ? 1 : b <= 32 ? 2 : 4;
-    if (fm == 2) {
-        fn = n / 128 >= 192 && m >= 8192 ? 8 : n / 32 >= 192 ? 2 : 1;
-        return true;
-    }
-    const int cap = fm == 1 ? 2 : 4;
-    for (fn = 1; fn < cap && n / (32 * fn) >= 192; fn *= 2) {}
-    return true;
-}
-
 hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream) {
     if (a.b == 0 || a.n == 0) return hipSuccess;
     if (a.tks > 1 && (a.acc || a.lr4 || a.tks > dual_max_t_slices(a.b, a.m, a.n, a.r))) return hipErrorInvalidValue;
@@ -1011,13 +988,6 @@ hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream) {
     }
     if (fn == 1) return launch_decode<1, 4, 2, 8>(a, stream);
     return fn == 2 ? launch_decode<2, 4, 2, 8>(a, stream) : launch_decode<4, 4, 1, 8>(a, stream);
-}
-
-int dual_max_t_slices(int64_t b, int64_t m, int64_t n, int r) {
-    int fn, fm;
-    if (r == 0 || !decode_shape(b, m, n, fn, fm) || fn * fm > 4) return 1;  // the epilogue reads T whole
-    const int rs = r <= 32 ? 1 : r <= 64 ? 2 : r <= 128 ? 4 : 8;
-    return kMaxTSlices / rs;
 }
 
 }  // namespace twq

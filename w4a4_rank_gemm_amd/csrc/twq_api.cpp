@@ -451,6 +451,30 @@ twq_status twq_debug_linear_lr4_main(const void *x, const void *qw, const float 
                            "twq_debug_linear_lr4_main", true);
 }
 
+// ---- offline fold (page 1, section 4.1) ----
+
+size_t twq_fold_workspace_bytes(int64_t m, int64_t n, int64_t r) {
+    if (m <= 0 || n <= 0 || r < 0 || r > kMaxRank || r > m || r > n || m > kMaxM || n > kMaxN) return 0;
+    return twq::fold_layout(m, n, r).total;
+}
+
+twq_status twq_fold_lowrank(const double *w, const double *u, const double *s, const double *vt, const double *q,
+                            const double *g, int64_t m, int64_t n, int64_t r, void *l1t, void *l2t, float *w_res,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    if (m <= 0 || n <= 0 || r < 0 || r > kMaxRank || r > m || r > n || m > kMaxM || n > kMaxN) return TWQ_ERR_SHAPE;
+    if (!w || !w_res) return TWQ_ERR_NULL;
+    if (r > 0 && (!u || !s || !vt || !l1t || !l2t)) return TWQ_ERR_NULL;
+    if (!aligned16(w) || !aligned16(w_res) || (q && !aligned16(q)) || (g && !aligned16(g))) return TWQ_ERR_ALIGN;
+    if (r > 0 && (!aligned16(u) || !aligned16(s) || !aligned16(vt) || !aligned16(l1t) || !aligned16(l2t)))
+        return TWQ_ERR_ALIGN;
+    const size_t need = twq::fold_layout(m, n, r).total;  // 0 for r == 0
+    if (need > 0 && (!workspace || workspace_bytes < need)) return TWQ_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return TWQ_ERR_ALIGN;
+    twq::FoldArgs a{w, u, s, vt, q, r > 0 ? g : nullptr, m, n, r, l1t, l2t, w_res, workspace};
+    const hipError_t e = twq::launch_fold(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TWQ_OK : hip_fail(e, "twq_fold_lowrank");
+}
+
 size_t twq_linear_workspace_bytes(int64_t b, int64_t m, int64_t n, int64_t r) {
     if (!valid_b(b) || !valid_m(m) || !valid_n(n) || !valid_r(r)) return 0;
     return linear_layout(b, m, n, r, 0).total;

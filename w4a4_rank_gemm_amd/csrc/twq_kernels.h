@@ -91,9 +91,17 @@ struct DualArgs {
 
 hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream);
 
+// Most partial sums of T (K slices x 32-rank steps) one lane of a decode epilogue
+// holds; a shape with more slices gets T reduced first.
+constexpr int kMaxTSlices = 16;
+
 // Largest number of T partial-sum slices the dual launch for this shape adds itself
 // (1: it needs T whole).
 int dual_max_t_slices(int64_t b, int64_t m, int64_t n, int r);
+
+// Few-token tiling of the dual launch (plan.cpp): fn x fm blocks of 16 channels x 16
+// tokens per CTA; false for many tokens (the LDS-ring kernel).
+bool decode_shape(int64_t b, int64_t m, int64_t n, int &fn, int &fm);
 
 // ---- int4 low-rank variant ------------------------------------------------------------
 
@@ -117,6 +125,27 @@ int hip_error(hipError_t e, const char *where);
 // is not NULL, the exact H [b][r] (int32) as well.
 hipError_t launch_lowrank_requant(const uint8_t *qx, const float *sx, const uint8_t *ql1, const float *c, int r,
                                   uint8_t *qh, float *sh, int32_t *h, int64_t b, int64_t m, hipStream_t stream);
+
+// ---- offline fold of given transforms into the split (fold.hip) ------------------------
+
+struct FoldArgs {
+    const double *w;   // W^T [n][m] (W is the pages' m x n weight)
+    const double *u;   // [m][r] left singular vectors of W (top r)
+    const double *s;   // [r] singular values
+    const double *vt;  // [r][n] right singular vectors, transposed
+    const double *q;   // [m][m] orthogonal, or NULL (identity)
+    const double *g;   // [r][r] invertible, or NULL (identity)
+    int64_t m, n, r;
+    void *l1t;         // out fp16 [r][m]: U'^T
+    void *l2t;         // out fp16 [n][r]: V'^T
+    float *w_res;      // out fp32 [n][m]: R'^T
+    void *workspace;   // fold_layout(m, n, r).total bytes
+};
+struct FoldLayout {
+    size_t ur, vr, t1, aug, ginv, total;  // byte offsets of the fp64 scratch arrays
+};
+FoldLayout fold_layout(int64_t m, int64_t n, int64_t r);  // plan.cpp
+hipError_t launch_fold(const FoldArgs &a, hipStream_t stream);
 
 hipError_t launch_pack_lowrank(const uint16_t *l1t, const uint16_t *l2t, int r, int64_t m, int64_t n, uint8_t *ql1,
                                float *sl1, uint8_t *ql2, float *sl2, float *c, hipStream_t stream);

@@ -8,8 +8,11 @@ give U' = Q^-1 U G, V' = G^-1 V and R' = Q^-1 R, and the layer is fed X Q; the r
 product is unchanged, (X Q)(U' V' + R') = X W. Learning Q and G needs calibration data
 and is not part of this library: they come in as inputs.
 
-This runs once per layer, before serving, on the platform's dense linear algebra (fp64
-matrix products, QR and SVD); its outputs feed twq_pack_weight and the fused layer.
+Only the SVD runs on the platform's dense linear algebra (torch.linalg, fp64); the
+folding -- the scalings, Q^T U_r G, G^-1 (Gauss-Jordan) V_r, the fp16 rounding of the
+factors and R' = Q^T W - U' V' -- is libtwq's twq_fold_lowrank (HIP kernels, binary64).
+This runs once per layer, before serving; its outputs feed twq_pack_weight and the
+fused layer.
 """
 from __future__ import annotations
 
@@ -51,29 +54,44 @@ def fold_split(w_nm: torch.Tensor, r: int, q: torch.Tensor | None = None, g: tor
     if not 0 <= r <= min(m, n):
         raise ValueError(f"rank {r} must lie in [0, min(m, n) = {min(m, n)}]")
     dev = w_nm.device
-    w = w_nm.to(torch.float64).T.contiguous()  # m x n
     if q is not None and q.shape != (m, m):
         raise ValueError("q must be [m][m]")
     if g is not None and g.shape != (r, r):
         raise ValueError("g must be [r][r]")
-    qt = None if q is None else q.to(dev, torch.float64).T
-    w_rot = w if qt is None else qt @ w
-    if r == 0:
-        return (torch.empty((0, m), dtype=torch.float16, device=dev), torch.empty((n, 0), dtype=torch.float16, device=dev),
-                w_rot.T.to(torch.float32).contiguous())
+    w_nm64 = w_nm.to(torch.float64).contiguous()
     if method == "auto":
         method = "exact" if max(m, n) <= 4096 else "randomized"
-    u, s, vt = _top_svd(w, r, method, seed)
-    rs = torch.sqrt(s)
-    u_r = u * rs[None, :]
-    v_r = rs[:, None] * vt
-    if qt is not None:
-        u_r = qt @ u_r
-    if g is not None:
-        gd = g.to(dev, torch.float64)
-        u_r = u_r @ gd
-        v_r = torch.linalg.solve(gd, v_r)
-    u_f = u_r.to(torch.float16)
-    v_f = v_r.to(torch.float16)
-    r_f = (w_rot - u_f.to(torch.float64) @ v_f.to(torch.float64)).to(torch.float32)
-    return u_f.T.contiguous(), v_f.T.contiguous(), r_f.T.contiguous()
+    if r > 0:  # the SVD of W (m x n) on the platform library
+        u, sv, vt = _top_svd(w_nm64.T, r, method, seed)
+        u, sv, vt = u.contiguous(), sv.contiguous(), vt.contiguous()
+    else:
+        u = sv = vt = None
+    qd = None if q is None else q.to(dev, torch.float64).contiguous()
+    gd = None if (g is None or r == 0) else g.to(dev, torch.float64).contiguous()
+    return fold_lowrank(w_nm64, u, sv, vt, qd, gd, r)
+
+
+def fold_lowrank(w_nm64: torch.Tensor, u, sv, vt, q, g, r: int):
+    """twq_fold_lowrank: the folded split from the top-r SVD factors of W (u fp64 [m][r],
+    sv [r], vt [r][n]; None when r == 0), W^T fp64 [n][m], and q fp64 [m][m] / g fp64
+    [r][r] or None. Returns (l1t' fp16 [r][m], l2t' fp16 [n][r], w_res' fp32 [n][m])."""
+    import w4a4_rank_gemm_amd as twq
+    n, m = w_nm64.shape
+    dev = w_nm64.device
+    for name, t, shape in (("w", w_nm64, (n, m)), ("u", u, (m, r)), ("s", sv, (r,)), ("vt", vt, (r, n)),
+                           ("q", q, (m, m)), ("g", g, (r, r))):
+        if t is None:
+            continue
+        if t.dtype != torch.float64 or not t.is_contiguous() or t.device != dev or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be contiguous fp64 {shape} on {dev}")
+    l1t = torch.empty((r, m), dtype=torch.float16, device=dev)
+    l2t = torch.empty((n, r), dtype=torch.float16, device=dev)
+    w_res = torch.empty((n, m), dtype=torch.float32, device=dev)
+    L = twq.lib()
+    need = L.twq_fold_workspace_bytes(m, n, r)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    P = twq._ptr
+    twq._check(L.twq_fold_lowrank(P(w_nm64), P(u), P(sv), P(vt), P(q), P(g), m, n, r, P(l1t) if r else None,
+                                  P(l2t) if r else None, P(w_res), P(ws), need, twq._stream(dev)),
+               "twq_fold_lowrank")
+    return l1t, l2t, w_res
