@@ -38,6 +38,13 @@ namespace twq {
 hipError_t launch_act(const ActArgs &a, const ActPlan &pl, hipStream_t) {
     if (a.b == 0) return hipSuccess;
     const size_t b = (size_t)a.b, m = (size_t)a.m, r = (size_t)a.r;
+    // the quantizer's share of the grid: nsl >= 1 CTAs a row (1 with many tokens); 1,
+    // 2, 4 or 8 chunks of 8 elements a thread covering the row over 256 threads, or 0
+    // for rows past 16384 elements
+    if (pl.nsl < 1 || (pl.mode == 0 && pl.nsl != 1)) return hipErrorInvalidValue;
+    if (pl.jq != 0 && pl.jq != 1 && pl.jq != 2 && pl.jq != 4 && pl.jq != 8) return hipErrorInvalidValue;
+    if (pl.jq ? (size_t)pl.jq * 256 * 8 < m || (pl.jq > 1 && (size_t)pl.jq * 128 * 8 >= m) : m <= 16384)
+        return hipErrorInvalidValue;
     touch_read(a.x, b * m * 2);
     touch_write(a.qx, a.a8 ? b * m : b * m / 2);
     touch_write(a.sx, (a.group ? m / a.group : 1) * b * 4);

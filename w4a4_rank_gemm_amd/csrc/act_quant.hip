@@ -4,8 +4,8 @@
 //  * per-token quantization (TwinQuant page 1, section 2, eq. (1)): a CTA of 256
 //    threads computes amax over a token row with a wave reduction, s_X =
 //    amax / 7, and the packed 4-bit codes of its slice of the row (few tokens:
-//    several CTAs per row); short rows stay in registers between the two passes,
-//    long rows are re-read from cache;
+//    several CTAs per row); rows up to 16384 elements stay in registers between
+//    the two passes, longer rows are re-read from cache;
 //  * the first low-rank product T = X L1 of eq. (3) on fp16 matrix cores with
 //    fp32 accumulation, cut into K slices so the read of X and L1 is spread over
 //    many compute units (one unit streams only tens of GB/s from HBM). A second,
@@ -18,13 +18,13 @@
 namespace twq {
 
 constexpr int kActThreads = 256;
-constexpr int kActMaxJ = 8;   // rows of up to 256 * 8 * 8 = 16384 fp16 stay in registers
 
 struct ActDev {
     int mode;        // 0: tiles of 128 token rows x all ranks; 1: all tokens x 16 ranks x a K slice
     int row_tile, ks, row_tiles, n_t_ctas;
     int fm;          // mode 1: token tiles of 16 (b <= 128)
     int nsl;         // CTAs per token row for the quantizer
+    int jq;          // chunks of a row per thread (0: rows past 16384 elements)
 };
 
 __device__ __forceinline__ uint32_t absmax8_bits(const uint4 c, uint32_t mx) {
@@ -64,56 +64,133 @@ __device__ __forceinline__ uint2 quant8_a8(const uint4 c, float s, float inv) {
     return make_uint2(out[0], out[1]);
 }
 
-// Slice sl (of nsl) of one token row, by one CTA of 256 threads: amax is taken over
-// the whole row (every slice reads it; only the first reads it from HBM), the codes
-// are written for the slice's chunks only. Spreading a short row over several
-// CTAs spreads its divisions over several compute units. A8: 8-bit codes
-// (q_max = 127), one byte each.
-template <bool A8>
-__device__ void quantize_row(const ActArgs &a, int64_t i, int sl, int nsl, uint32_t *red) {
-    const int tid = threadIdx.x;
-    const int64_t nch = a.m / 8;  // 16-byte chunks of 8 fp16
-    const int64_t c_lo = nch * sl / nsl, c_hi = nch * (sl + 1) / nsl;
+// The chunks of a row that thread tid holds: 16-byte chunk c = tid + 256 j of the row
+// (8 fp16), j < J, zero past the row's nch chunks. J is a compile-time count (a loop
+// of guarded loads sized at run time measured 0.6 us slower on a 4096-element row).
+template <int J>
+__device__ __forceinline__ void load_row(const ActArgs &a, int64_t i, uint4 (&v)[J]) {
     const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + i * a.m);
-    uint32_t *qr = reinterpret_cast<uint32_t *>(a.qx + i * (a.m / 2));
-    const bool cached = nch <= (int64_t)kActThreads * kActMaxJ;
-    uint4 v[kActMaxJ];
-    uint32_t mx = 0;
-    if (cached) {
+    const int64_t nch = a.m / 8;
 #pragma unroll
-        for (int j = 0; j < kActMaxJ; ++j) {
-            const int64_t c = tid + (int64_t)j * kActThreads;
-            v[j] = c < nch ? xr[c] : make_uint4(0, 0, 0, 0);
-            mx = absmax8_bits(v[j], mx);
-        }
-    } else {
-        for (int64_t c = tid; c < nch; c += kActThreads) mx = absmax8_bits(xr[c], mx);
+    for (int j = 0; j < J; ++j) {
+        const int64_t c = threadIdx.x + (int64_t)j * kActThreads;
+        v[j] = c < nch ? xr[c] : make_uint4(0, 0, 0, 0);
     }
-    mx = wave_max_u32(mx);
-    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = mx;
-    __syncthreads();
-    mx = red[0];
+}
+
+template <int J>
+__device__ __forceinline__ uint32_t row_absmax_bits(const uint4 (&v)[J]) {
+    uint32_t mx = 0;
 #pragma unroll
-    for (int w = 1; w < kActThreads / kWave; ++w) mx = mx > red[w] ? mx : red[w];
-    const float amax = half_bits_to_float(mx);
-    const float s = amax / (A8 ? kQMax8 : kQMax);  // correctly rounded binary32 division
-    const float inv = 1.0f / s;                     // only used when amax > 0
-    if (tid == 0 && sl == 0) a.sx[i] = s;
-    uint2 *qr8 = reinterpret_cast<uint2 *>(a.qx + i * a.m);
-    auto put = [&](int64_t c, const uint4 chunk) {
-        if constexpr (A8)
-            qr8[c] = amax == 0.0f ? make_uint2(0u, 0u) : quant8_a8(chunk, s, inv);
-        else
-            qr[c] = amax == 0.0f ? 0u : quant8(chunk, s, inv);
-    };
-    if (cached) {
+    for (int j = 0; j < J; ++j) mx = absmax8_bits(v[j], mx);
+    return wave_max_u32(mx);
+}
+
+// s_X of eq. (1) from the row's amax: the correctly rounded binary32 division
+__device__ __forceinline__ float row_scale(float amax, bool a8) { return amax / (a8 ? kQMax8 : kQMax); }
+
+// Chunk c (held in registers) of row i into its codes
+template <bool A8>
+__device__ __forceinline__ void put_chunk(const ActArgs &a, int64_t i, int64_t c, const uint4 chunk, float amax,
+                                          float s, float inv) {
+    if constexpr (A8)
+        reinterpret_cast<uint2 *>(a.qx + i * a.m)[c] = amax == 0.0f ? make_uint2(0u, 0u) : quant8_a8(chunk, s, inv);
+    else
+        reinterpret_cast<uint32_t *>(a.qx + i * (a.m / 2))[c] = amax == 0.0f ? 0u : quant8(chunk, s, inv);
+}
+
+// Few tokens: slice sl (of nsl) of token row i, by one CTA of 256 threads. amax is
+// taken over the whole row (every slice reads it; only the first reads it from HBM),
+// codes are written for the slice's chunks [c_lo, c_hi) only, so the divisions of a
+// short row are spread over several compute units. Where the slice is 64 or 128 chunks
+// it is staged in LDS (stage: 2 KB) beside the amax reduction, so that all 256 threads
+// take 2 or 4 codes each, instead of a quarter or a half of the threads taking 8
+// (measured on MI355X: the packing ran 0.5 us on one wave). J: chunks a thread holds,
+// J * 256 >= m / 8. A8: 8-bit codes (q_max = 127), one byte each.
+template <bool A8, int J>
+__device__ void quantize_slice(const ActArgs &a, int64_t i, int sl, int nsl, uint32_t *red, uint4 *stage) {
+    const int tid = threadIdx.x;
+    const int64_t nch = a.m / 8;
+    const int64_t c_lo = nch * sl / nsl, c_hi = nch * (sl + 1) / nsl, nc = c_hi - c_lo;
+    uint4 v[J];
+    load_row<J>(a, i, v);
+    const uint32_t mx = row_absmax_bits<J>(v);
+    if (tid % kWave == 0) red[tid / kWave] = mx;
+    const bool spread = nc == 64 || nc == 128;
+    if (spread) {
 #pragma unroll
-        for (int j = 0; j < kActMaxJ; ++j) {
+        for (int j = 0; j < J; ++j) {
             const int64_t c = tid + (int64_t)j * kActThreads;
-            if (c >= c_lo && c < c_hi) put(c, v[j]);
+            if (c >= c_lo && c < c_hi) stage[c - c_lo] = v[j];
         }
-    } else {
-        for (int64_t c = c_lo + tid; c < c_hi; c += kActThreads) put(c, xr[c]);
+    }
+    __syncthreads();
+    uint32_t m4 = red[0];
+#pragma unroll
+    for (int w = 1; w < kActThreads / kWave; ++w) m4 = m4 > red[w] ? m4 : red[w];
+    const float amax = half_bits_to_float(m4);
+    const float s = row_scale(amax, A8);
+    const float inv = 1.0f / s;  // only used when amax > 0
+    if (tid == 0 && sl == 0) a.sx[i] = s;
+    if (spread) {
+        // thread tid: elements tid K .. tid K + K - 1 of the slice, K = nc / 32
+        const uint16_t *st = reinterpret_cast<const uint16_t *>(stage);
+        int q[4] = {0, 0, 0, 0};
+        const int K = (int)(nc / 32);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (k < K && amax != 0.0f) {
+                const float x = half_bits_to_float(st[tid * K + k]);
+                q[k] = A8 ? quant_code8_fast(x, s, inv) : quant_code_fast(x, s, inv);
+            }
+        if constexpr (A8) {
+            uint8_t *dst = a.qx + i * a.m + c_lo * 8 + (int64_t)tid * K;
+            const uint32_t b01 = (uint32_t(q[0]) & 0xFFu) | ((uint32_t(q[1]) & 0xFFu) << 8);
+            if (K == 2)
+                *reinterpret_cast<uint16_t *>(dst) = (uint16_t)b01;
+            else
+                *reinterpret_cast<uint32_t *>(dst) = b01 | ((uint32_t(q[2]) & 0xFFu) << 16) | ((uint32_t(q[3]) & 0xFFu) << 24);
+        } else {
+            uint8_t *dst = a.qx + i * (a.m / 2) + c_lo * 4 + (int64_t)tid * (K / 2);
+            const uint32_t b0 = (uint32_t(q[0]) & 0xFu) | ((uint32_t(q[1]) & 0xFu) << 4);
+            if (K == 2)
+                *dst = (uint8_t)b0;
+            else
+                *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(b0 | (((uint32_t(q[2]) & 0xFu) | ((uint32_t(q[3]) & 0xFu) << 4)) << 8));
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int64_t c = tid + (int64_t)j * kActThreads;
+        if (c >= c_lo && c < c_hi) put_chunk<A8>(a, i, c, v[j], amax, s, inv);
+    }
+}
+
+// Rows longer than 256 * 8 chunks (m > 16384): amax in one pass over the row, the
+// codes of slice sl (of nsl) in a second, re-read from cache; rows q0, q0 + nq, ...
+// (the launch gives every CTA one row: nq = b).
+template <bool A8>
+__device__ void quantize_long_rows(const ActArgs &a, int64_t q0, int64_t nq, int sl, int nsl, uint32_t *red) {
+    const int tid = threadIdx.x;
+    const int64_t nch = a.m / 8;
+    const int64_t c_lo = nch * sl / nsl, c_hi = nch * (sl + 1) / nsl;
+    for (int64_t i = q0; i < a.b; i += nq) {
+        const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + i * a.m);
+        uint32_t mx = 0;
+        for (int64_t c = tid; c < nch; c += kActThreads) mx = absmax8_bits(xr[c], mx);
+        mx = wave_max_u32(mx);
+        if (tid % kWave == 0) red[tid / kWave] = mx;
+        __syncthreads();
+        uint32_t m4 = red[0];
+#pragma unroll
+        for (int w = 1; w < kActThreads / kWave; ++w) m4 = m4 > red[w] ? m4 : red[w];
+        __syncthreads();  // every wave has read red before the next row writes it
+        const float amax = half_bits_to_float(m4);
+        const float s = row_scale(amax, A8);
+        const float inv = 1.0f / s;
+        if (tid == 0 && sl == 0) a.sx[i] = s;
+        for (int64_t c = c_lo + tid; c < c_hi; c += kActThreads) put_chunk<A8>(a, i, c, xr[c], amax, s, inv);
     }
 }
 
@@ -302,11 +379,30 @@ __device__ void t_slices(const ActArgs &a, const ActDev &p, int tb, float *lds) 
     }
 }
 
+// Quantizer CTA q: token row q / nsl, slice q % nsl (many tokens: nsl = 1). One CTA
+// per row measured faster at prefill than a few CTAs per compute unit looping over
+// rows in batches (b = m = 8192: 81 against 100-117 us for the whole launch, with 256
+// to 2048 looping CTAs; likewise on the gate/up and down shapes).
+template <bool A8>
+__device__ void quantize_part(const ActArgs &a, const ActDev &p, int64_t q, uint32_t *red, float *lds) {
+    const int64_t i = q / p.nsl;
+    const int sl = (int)(q % p.nsl);
+    uint4 *stage = reinterpret_cast<uint4 *>(lds);  // the T tiles' buffer: quantizer CTAs compute no T
+    switch (p.jq) {
+        case 1: quantize_slice<A8, 1>(a, i, sl, p.nsl, red, stage); return;
+        case 2: quantize_slice<A8, 2>(a, i, sl, p.nsl, red, stage); return;
+        case 4: quantize_slice<A8, 4>(a, i, sl, p.nsl, red, stage); return;
+        case 8: quantize_slice<A8, 8>(a, i, sl, p.nsl, red, stage); return;
+        default: quantize_long_rows<A8>(a, i, a.b, sl, p.nsl, red); return;
+    }
+}
+
 // Many tokens (MODE 0): T partials by t_tiles<NT = r / 16>. Few tokens (MODE 1): T
 // partials by t_slices<NT = FM>. The remaining CTAs quantize, nsl CTAs per token row.
 template <int MODE, int NT>
 __global__ __launch_bounds__(kActThreads) void act_kernel(ActArgs a, ActDev p) {
-    __shared__ float lds[MODE == 1 ? 3 * NT * kWave * 4 : 1];
+    // MODE 1: T's wave sums, or a quantizer CTA's staged slice (128 chunks)
+    __shared__ __attribute__((aligned(16))) float lds[MODE == 1 ? (3 * NT * kWave * 4 > 512 ? 3 * NT * kWave * 4 : 512) : 512];
     __shared__ __attribute__((aligned(16))) uint8_t ring[MODE == 0 ? 3 * (128 + 16 * ((NT + 3) / 4 * 4)) * 64 : 16];
     __shared__ uint32_t red[kActThreads / kWave];
     const int64_t bid = blockIdx.x;
@@ -320,9 +416,9 @@ __global__ __launch_bounds__(kActThreads) void act_kernel(ActArgs a, ActDev p) {
         if (a.group)
             quantize_row_grouped(a, q / p.nsl, (int)(q % p.nsl), p.nsl);
         else if (a.a8)
-            quantize_row<true>(a, q / p.nsl, (int)(q % p.nsl), p.nsl, red);
+            quantize_part<true>(a, p, q, red, lds);
         else
-            quantize_row<false>(a, q / p.nsl, (int)(q % p.nsl), p.nsl, red);
+            quantize_part<false>(a, p, q, red, lds);
     }
 }
 
@@ -390,6 +486,7 @@ hipError_t launch_act(const ActArgs &a, const ActPlan &pl, hipStream_t stream) {
     p.ks = pl.ks;
     p.row_tiles = pl.row_tiles;
     p.nsl = pl.nsl;
+    p.jq = pl.jq;
     p.n_t_ctas = a.r > 0 ? pl.row_tiles * pl.ks : 0;
     const int64_t grid = p.n_t_ctas + a.b * pl.nsl;
     const bool ok = pl.mode == 0 ? launch_nt<0>(a.r / 16, a, p, grid, stream)

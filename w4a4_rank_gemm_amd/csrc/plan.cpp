@@ -49,6 +49,9 @@ ActPlan plan_act(int64_t b, int64_t m, int64_t r) {
         while (b * nsl < 128 && (m / 8) / (nsl * 2) >= 32) nsl *= 2;
         pl.nsl = (int)nsl;
     }
+    // a row of m fp16 is m / 8 chunks of 16 bytes over 256 threads
+    const int64_t per_thread = (m / 8 + 255) / 256;
+    pl.jq = per_thread <= 1 ? 1 : per_thread <= 2 ? 2 : per_thread <= 4 ? 4 : per_thread <= 8 ? 8 : 0;
     if (r > 0 && pl.ks > 1) {
         const int64_t rows_pad = pl.mode == 0 ? (int64_t)pl.row_tiles * 128 : (int64_t)pl.fm * 16;
         pl.workspace_bytes = (size_t)pl.ks * rows_pad * r * sizeof(float);

@@ -21,6 +21,7 @@ struct ActPlan {
     int ks;          // K slices; 1 means T is written directly
     int row_tiles;   // mode 0: ceil(b / 128) row tiles; mode 1: r / 16 rank tiles
     int nsl;         // CTAs per token row for the quantizer
+    int jq;          // 16-byte chunks of a row each thread holds: 1, 2, 4 or 8 (m <= 16384), else 0
     size_t workspace_bytes;  // partial sums of T: ks slices of [row_tiles * 128 or 16 fm][r] floats
 };
 
