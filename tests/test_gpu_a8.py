@@ -63,6 +63,8 @@ SHAPES = [
     (16, 512, 16384, 16), (5, 2048, 16384, 64), (300, 4096, 1040, 32), (27, 512, 8208, 48),
     # wide few-token grids: 2x2 and 4x4 blocks of 16 per CTA, a partial last channel tile
     (27, 384, 24592, 32), (64, 256, 12304, 48), (48, 512, 8192, 32),
+    # rows past 16384 elements (two-pass quantizer) and 128-chunk few-token slices
+    (3, 32768, 48, 32), (130, 20480, 80, 16), (16, 8192, 96, 32),
 ]
 
 

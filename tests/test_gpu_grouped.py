@@ -78,6 +78,8 @@ SHAPES = [
     (27, 384, 24592, 32), (64, 256, 12304, 48), (48, 512, 8192, 32),
     # tilings that read Q_X from LDS at m <= 4096: 2x1, 2x2 and 4x4 blocks, ragged tokens
     (9, 2048, 8192, 32), (30, 3072, 24576, 32), (61, 640, 12304, 16),
+    # rows past 16384 elements, few and many tokens
+    (3, 32768, 48, 32), (130, 20480, 80, 16),
 ]
 
 

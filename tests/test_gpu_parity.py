@@ -145,6 +145,9 @@ RAGGED = [
     # per wave: 1x2 and 1x4 blocks of eight waves, 2x4, 2x2 of four waves, 8x2 at m = 8192
     (20, 1536, 1040, 32), (40, 3072, 2000, 48), (57, 2560, 6160, 16), (31, 4096, 9008, 64),
     (50, 1152, 12304, 32), (29, 8192, 24592, 32),
+    # rows past 16384 elements (the quantizer's two-pass path, few and many tokens) and
+    # few-token slices of 128 chunks staged through LDS
+    (3, 32768, 48, 32), (16, 16512, 64, 16), (130, 20480, 80, 16), (16, 8192, 96, 32),
 ]
 
 
