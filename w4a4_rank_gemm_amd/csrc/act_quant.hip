@@ -222,16 +222,21 @@ __device__ void quantize_row_grouped(const ActArgs &a, int64_t i, int sl, int ns
 // T tile for many tokens: tokens [128 tm, 128 tm + 128) x all r = 16 NR ranks over K
 // slice ks, in steps of 32 (64 bytes of fp16 per row). The step's 128 X rows and its
 // L1^T rows (NR blocks of 16, padded to a multiple of four blocks with clamped rows)
-// go through a three-slot LDS ring filled by direct-to-LDS buffer loads, laid out as
-// the prefill main loop's ring: 16-row blocks, rows 2s and 2s + 1 sharing 128-byte
-// line s with the 16-byte chunk index XORed by s, which makes the loads coalesce and
-// the operand reads conflict-free. X rows are read from HBM once and L1 rows once per
-// CTA. Wave w owns tokens [32 w, 32 w + 32) x all ranks: A = L1^T block (16 ranks),
-// B = X block (16 tokens), so lane (li, g) ends with ranks 4g..4g+3 of token li.
+// go through an LDS ring filled by direct-to-LDS buffer loads, laid out as the prefill
+// main loop's ring: 16-row blocks, rows 2s and 2s + 1 sharing 128-byte line s with the
+// 16-byte chunk index XORed by s, which makes the loads coalesce and the operand reads
+// conflict-free. X rows are read from HBM once and L1 rows once per CTA. Wave w owns
+// tokens [32 w, 32 w + 32) x all ranks: A = L1^T block (16 ranks), B = X block (16
+// tokens), so lane (li, g) ends with ranks 4g..4g+3 of token li. The ring has three
+// slots up to 64 ranks (37 KB) and two above (32-56 KB instead of 49-74 KB): every
+// CTA of the launch holds the ring, the quantizer CTAs included, and the smaller ring
+// leaves them more slots a compute unit. Measured on MI355X at b = m = 8192, r = 128:
+// the T tiles alone take 52 us instead of 33, but the whole launch 74 instead of 79,
+// and the benchmark call 1369-1377 us instead of 1380-1384.
 template <int NR>
 __device__ void t_tiles(const ActArgs &a, const ActDev &p, int tb, uint8_t *ring) {
     constexpr int BM = 128, NRP = (NR + 3) / 4 * 4, ROWS = BM + 16 * NRP;
-    constexpr int S = 3, BLK = 1024, STAGE = ROWS * 64, DPT = ROWS * 4 / kActThreads;
+    constexpr int S = NR > 4 ? 2 : 3, BLK = 1024, STAGE = ROWS * 64, DPT = ROWS * 4 / kActThreads;
     static_assert(ROWS * 4 % kActThreads == 0 && BM * 4 % kActThreads == 0, "DMA groups");
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int li = lane & 15, g = lane >> 4;
@@ -403,7 +408,8 @@ template <int MODE, int NT>
 __global__ __launch_bounds__(kActThreads) void act_kernel(ActArgs a, ActDev p) {
     // MODE 1: T's wave sums, or a quantizer CTA's staged slice (128 chunks)
     __shared__ __attribute__((aligned(16))) float lds[MODE == 1 ? (3 * NT * kWave * 4 > 512 ? 3 * NT * kWave * 4 : 512) : 512];
-    __shared__ __attribute__((aligned(16))) uint8_t ring[MODE == 0 ? 3 * (128 + 16 * ((NT + 3) / 4 * 4)) * 64 : 16];
+    // T tiles' ring: slots (3, or 2 above 64 ranks) x (128 token rows + the rank rows) x 64 bytes
+    __shared__ __attribute__((aligned(16))) uint8_t ring[MODE == 0 ? (NT > 4 ? 2 : 3) * (128 + 16 * ((NT + 3) / 4 * 4)) * 64 : 16];
     __shared__ uint32_t red[kActThreads / kWave];
     const int64_t bid = blockIdx.x;
     if (bid < p.n_t_ctas) {
