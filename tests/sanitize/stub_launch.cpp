@@ -56,7 +56,10 @@ hipError_t launch_act(const ActArgs &a, const ActPlan &pl, hipStream_t) {
         touch_write(a.partials, (size_t)pl.ks * rows_pad * r * 4);
         if (a.keep_partials) return hipSuccess;
     }
-    touch_write(a.t, b * r * 4);
+    if (a.t16)
+        touch_write(a.t16, b * r * 2);
+    else
+        touch_write(a.t, b * r * 4);
     return hipSuccess;
 }
 
@@ -86,6 +89,8 @@ hipError_t launch_dual_linear(const DualArgs &a, hipStream_t) {
             // slice s of T's partial sums starts at s * tstride floats
             if ((size_t)a.tstride < b * r) return hipErrorInvalidValue;
             touch_read(a.tpart, ((size_t)(a.tks - 1) * (size_t)a.tstride + b * r) * 4);
+        } else if (a.t16) {
+            touch_read(a.t16, b * r * 2);  // T already fp16 (many tokens, T reduced from slices)
         } else {
             touch_read(a.t, b * r * 4);
         }

@@ -431,9 +431,11 @@ __global__ __launch_bounds__(kActThreads) void act_kernel(ActArgs a, ActDev p) {
 // T[row][c] = sum over slices s (in slice order) of partials[s][row][c]. The data is
 // small and the kernel latency-bound, so every load of a thread is issued before any
 // is added (KS_MAX slices in flight; loads past ks re-read slice 0 and are not added).
+// t16: T is stored rounded to fp16 (nearest even, the rounding the fused epilogue
+// applies to T) instead of in fp32.
 template <int KS_MAX>
 __global__ __launch_bounds__(256) void t_reduce_kernel(const float *partials, int64_t b, int64_t rows_pad,
-                                                       int r, int ks, float *t) {
+                                                       int r, int ks, float *t, uint16_t *t16) {
     const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 index into T
     const int64_t n4 = b * r / 4;
     if (i4 >= n4) return;
@@ -446,7 +448,14 @@ __global__ __launch_bounds__(256) void t_reduce_kernel(const float *partials, in
 #pragma unroll
     for (int u = 1; u < KS_MAX; ++u)
         if (u < ks) sum += v[u];
-    *reinterpret_cast<v4f *>(t + i4 * 4) = sum;
+    if (t16) {
+        v4h h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = (_Float16)sum[e];
+        *reinterpret_cast<v4h *>(t16 + i4 * 4) = h;
+    } else {
+        *reinterpret_cast<v4f *>(t + i4 * 4) = sum;
+    }
 }
 
 template <int MODE, int NT>
@@ -504,11 +513,11 @@ hipError_t launch_act(const ActArgs &a, const ActPlan &pl, hipStream_t stream) {
     const int64_t rows_pad = pl.mode == 0 ? (int64_t)pl.row_tiles * 128 : (int64_t)pl.fm * 16;
     const dim3 rgrid((unsigned)((n4 + 255) / 256));
     if (pl.ks <= 8)
-        hipLaunchKernelGGL(t_reduce_kernel<8>, rgrid, dim3(256), 0, stream, a.partials, a.b, rows_pad, a.r, pl.ks, a.t);
+        hipLaunchKernelGGL(t_reduce_kernel<8>, rgrid, dim3(256), 0, stream, a.partials, a.b, rows_pad, a.r, pl.ks, a.t, a.t16);
     else if (pl.ks <= 16)
-        hipLaunchKernelGGL(t_reduce_kernel<16>, rgrid, dim3(256), 0, stream, a.partials, a.b, rows_pad, a.r, pl.ks, a.t);
+        hipLaunchKernelGGL(t_reduce_kernel<16>, rgrid, dim3(256), 0, stream, a.partials, a.b, rows_pad, a.r, pl.ks, a.t, a.t16);
     else if (pl.ks <= 32)
-        hipLaunchKernelGGL(t_reduce_kernel<32>, rgrid, dim3(256), 0, stream, a.partials, a.b, rows_pad, a.r, pl.ks, a.t);
+        hipLaunchKernelGGL(t_reduce_kernel<32>, rgrid, dim3(256), 0, stream, a.partials, a.b, rows_pad, a.r, pl.ks, a.t, a.t16);
     else
         return hipErrorInvalidValue;  // plan_act keeps ks <= 32
     return hipGetLastError();

@@ -610,12 +610,110 @@ static hipError_t launch_decode(const DualArgs &a, hipStream_t stream) {
 // groups of GM token tiles, so the CTAs an XCD runs at once share W and Q_X tiles in
 // that XCD's L2.
 
+// Y of a wave's FN x FM tiles, stored fp16 (rows past n or b not stored).
+template <int BN, int BM, int WN, int WM, int FN, int FM>
+__device__ __forceinline__ void pf_store(const DualArgs &a, const v4f (&y)[FN][FM], int64_t ch0, int64_t tok0, int wn,
+                                         int wm, int li, int g) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + 4 * g;
+            const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
+            if (ch < a.n && tok < a.b) {
+                v4h o;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) o[v] = (_Float16)y[fn][fm][v];
+                *reinterpret_cast<v4h *>(a.y + tok * a.n + ch) = o;
+            }
+        }
+}
+
+// The fp16 low-rank branch with its operands staged through the CTA's LDS ring (T as
+// fp16, a.t16). A step of 32 ranks needs the tile's BN rows of L2^T and BM rows of T,
+// 64 bytes each: the shape of one main-loop stage, so it is loaded, laid out and read
+// exactly as one (direct-to-LDS loads, two slots, the next step in flight while this one
+// is used), and no register holds a load in flight. Measured on MI355X at b = m = 8192,
+// n = 28672, r = 128: this branch cost 98 us of the 1306 us kernel with its operands
+// loaded into registers step by step (four round trips per tile); the ring hides all but
+// the first. The buffers' record counts are the operands' exact sizes, so the half step
+// past r (r an odd multiple of 16) of the last row reads zeros; other rows' dead ranks are
+// zeroed below, as in the register path. The sums are the register path's, in the same
+// order, on the same fp16 values: Y is the same bit for bit.
+template <int BN, int BM, int WN, int WM, int SLOT, int FN, int FM>
+__device__ __forceinline__ void pf_lowrank_lds(const DualArgs &a, v4f (&y)[FN][FM], int64_t ch0, int64_t tok0, int wn,
+                                               int wm, int li, int g, uint8_t *ring, int tid) {
+    constexpr int NT = WN * WM * 64, CPR = 4, BLK = 1024, ROWS = BN + BM, DPT = ROWS * CPR / NT;
+    static_assert(ROWS * 64 <= SLOT && (BN * CPR) % NT == 0 && FN == 4 && FM == 4, "one step fits a ring slot");
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int nst = (a.r + 31) / 32;
+    // this thread's loads of a step: the main loop's (row, 16-byte chunk) mapping, rows of
+    // L2^T (channel rows, first BN) or of T (token rows), clamped into the operand
+    uint32_t off[DPT];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+        const int q = j * NT + tid;
+        const int line = (q % 64) / 8, logical = (q % 8) ^ line;
+        const int row = (q / 64) * 16 + 2 * line + logical / 4, chunk = logical % 4;
+        const int64_t rr = row < BN ? (ch0 + row < a.n ? ch0 + row : a.n - 1)
+                                    : (tok0 + row - BN < a.b ? tok0 + row - BN : a.b - 1);
+        off[j] = (uint32_t)(rr * a.r * 2 + chunk * 16);
+    }
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.l2t), 0,
+                                                                        (int)(a.n * a.r * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.t16), 0,
+                                                                        (int)(a.b * a.r * 2), 0x00020000);
+    auto issue = [&](int st, auto slot) {
+        uint8_t *dst = ring + decltype(slot)::value * SLOT;
+        const int sc = st < nst ? st : nst - 1;  // past the last step: reloaded, unused
+#pragma unroll
+        for (int j = 0; j < DPT; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((j * NT) / CPR < BN ? rl : rt,
+                                                     (__attribute__((address_space(3))) void *)(dst + (j * NT + wave * kWave) * 16),
+                                                     16, (int)off[j], sc * 64, 0, 0);
+    };
+    // operand reads: row li, chunk g of a block, as in the main loop
+    const uint32_t lane_off = (li / 2) * 128 + ((4 * (li % 2) + g) ^ (li / 2)) * 16;
+    const uint32_t rda = lds_offset(ring) + lane_off + (wn * (BN / WN) / 16) * BLK;
+    const uint32_t rdb = lds_offset(ring) + lane_off + ((BN + wm * (BM / WM)) / 16) * BLK;
+
+    // the main loop's look-ahead loads (its last steps reload the last stage into slots no
+    // step reads) must have landed before these slots are refilled: drain them, then meet
+    wait_vmcnt<0>();
+    stage_barrier();  // every wave is done with the main loop's last stage
+    issue(0, std::integral_constant<int, 0>{});
+    issue(1, std::integral_constant<int, 1>{});
+    for (int s0 = 0; s0 < nst; s0 += 2) {
+        static_for(std::make_integer_sequence<int, 2>{}, [&](auto u) {
+            const int st = s0 + u;
+            if (st >= nst) return;
+            wait_vmcnt<DPT>();  // step st landed for this thread (step st + 1 may be in flight)
+            stage_barrier();    // ... and for every thread
+            v4i raw[8];
+            lds_read_4x4<decltype(u)::value * SLOT, BLK>(rda, rdb, raw);
+            const bool live = st * 32 + g * 8 < a.r;  // r is a multiple of 16
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    y[fn][fm] = mfma_f16(__builtin_bit_cast(v8h, raw[fn]), live ? __builtin_bit_cast(v8h, raw[4 + fm]) : v8h{},
+                                         y[fn][fm]);
+            stage_barrier();  // every wave is done with this slot
+            issue(st + 2, u);
+        });
+    }
+    wait_vmcnt<0>();  // no load may still be writing this CTA's LDS when it ends
+}
+
 // Second half of the many-token epilogue, from the dequantized residual y of a wave's
 // FN x FM tiles of 16 x 16 (the wave at (wn, wm) of a BN x BM CTA tile at (ch0, tok0)):
 // add the low-rank branch and store fp16.
-template <int BN, int BM, int WN, int WM, bool LR4, int FN, int FM>
+// SLOT > 0: T comes as fp16 (a.t16), and the CTA's LDS ring (two slots of SLOT bytes, free
+// once the main loop is done) carries the low-rank operands, see pf_lowrank_lds. A
+// compile-time choice: with both paths in one kernel the four-CTA kernel spilled.
+template <int BN, int BM, int WN, int WM, bool LR4, int SLOT, int FN, int FM>
 __device__ __forceinline__ void pf_finish(const DualArgs &a, v4f (&y)[FN][FM], int64_t ch0, int64_t tok0, int wn, int wm,
-                                          int li, int g) {
+                                          int li, int g, uint8_t *ring, int tid) {
     if constexpr (LR4) {
         // int4 low-rank branch: y += s_H (Q_H Q_L2^T)
         if (a.r > 0) {
@@ -635,6 +733,13 @@ __device__ __forceinline__ void pf_finish(const DualArgs &a, v4f (&y)[FN][FM], i
     // fp16 low-rank branch: y += L2^T (channels x ranks) . T^T (ranks x tokens). Rows are
     // addressed by 32-bit element offsets from the uniform bases (n r and b r stay below
     // 2^32 within the ABI's limits) rather than one 64-bit pointer per row.
+    if constexpr (SLOT > 0 && !LR4) {
+        if (a.r > 0) {
+            pf_lowrank_lds<BN, BM, WN, WM, SLOT>(a, y, ch0, tok0, wn, wm, li, g, ring, tid);
+            pf_store<BN, BM, WN, WM>(a, y, ch0, tok0, wn, wm, li, g);
+            return;
+        }
+    }
     const int64_t chb = ch0 + wn * (BN / WN) + li, tkb = tok0 + wm * (BM / WM) + li;
     for (int k0 = 0; k0 < (LR4 ? 0 : a.r); k0 += 32) {
         const int rank = k0 + g * 8;
@@ -657,27 +762,15 @@ __device__ __forceinline__ void pf_finish(const DualArgs &a, v4f (&y)[FN][FM], i
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) y[fn][fm] = mfma_f16(la[fn], tb[fm], y[fn][fm]);
     }
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int64_t ch = ch0 + wn * (BN / WN) + fn * 16 + 4 * g;
-            const int64_t tok = tok0 + wm * (BM / WM) + fm * 16 + li;
-            if (ch < a.n && tok < a.b) {
-                v4h o;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) o[v] = (_Float16)y[fn][fm][v];
-                *reinterpret_cast<v4h *>(a.y + tok * a.n + ch) = o;
-            }
-        }
+    pf_store<BN, BM, WN, WM>(a, y, ch0, tok0, wn, wm, li, g);
 }
 
 // Epilogue of the many-token kernels: dequantize the integer sums, then pf_finish (or
 // store the exact integer sums). SH: log2 of the operands' combined scale in acc (8 for
 // 4-bit x 4-bit, 4 for W4A8).
-template <int BN, int BM, int WN, int WM, bool STORE_ACC, bool LR4, int SH, int FN, int FM>
+template <int BN, int BM, int WN, int WM, bool STORE_ACC, bool LR4, int SH, int SLOT, int FN, int FM>
 __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM], int64_t ch0, int64_t tok0, int wn, int wm,
-                                            int li, int g) {
+                                            int li, int g, uint8_t *ring, int tid) {
     // lane (li, g), register v of tile (fn, fm) holds channel ch_base + 4g + v, token tok_base + li
     if constexpr (STORE_ACC) {
 #pragma unroll
@@ -706,7 +799,7 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 #pragma unroll
                 for (int v = 0; v < 4; ++v) y[fn][fm][v] = (sxv[fm] * swv[v]) * (float)(acc[fn][fm][v] >> SH);
         }
-        pf_finish<BN, BM, WN, WM, LR4>(a, y, ch0, tok0, wn, wm, li, g);
+        pf_finish<BN, BM, WN, WM, LR4, SLOT>(a, y, ch0, tok0, wn, wm, li, g, ring, tid);
     }
 }
 
@@ -734,7 +827,7 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 // gave lanes g and g + 2 the same banks: LDS bank conflicts, 2-3.6% slower), permuted
 // into the expanded weight operand's lane order (perm16); the accumulator holds 16 acc.
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false,
-          bool A8 = false>
+          bool A8 = false, bool T16 = false>
 __global__ __launch_bounds__(WN * WM * 64, A8 ? (S > 2 ? 2 : 3) : (S == 2 ? 4 : 3))
 void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     constexpr int NT = WN * WM * 64;
@@ -754,6 +847,7 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     static_assert(!GRP || (RB == 64 && BN == 128 && BM == 128 && NT == 256 && !STORE_ACC && !LR4),
                   "group-wise: one group per stage, one scale load per thread");
 
+    static_assert(!T16 || (!A8 && !LR4 && !STORE_ACC && RB == 64), "fp16 T through the ring: 64-byte stages");
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int li = lane & 15, g = lane >> 4;
     const int wn = wave % WN, wm = wave / WN;
@@ -936,16 +1030,17 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     const int li_e = te & 15, g_e = (te >> 4) & 3;
     const int wn_e = wave_u % WN, wm_e = wave_u / WN;
     if constexpr (GRP)
-        pf_finish<BN, BM, WN, WM, false>(a, yg, ch0, tok0, wn_e, wm_e, li_e, g_e);
+        pf_finish<BN, BM, WN, WM, false, T16 ? SLOT : 0>(a, yg, ch0, tok0, wn_e, wm_e, li_e, g_e, ring, te);
     else
-        pf_epilogue<BN, BM, WN, WM, STORE_ACC, LR4, A8 ? 4 : 8>(a, acc, ch0, tok0, wn_e, wm_e, li_e, g_e);
+        pf_epilogue<BN, BM, WN, WM, STORE_ACC, LR4, A8 ? 4 : 8, T16 ? SLOT : 0>(a, acc, ch0, tok0, wn_e, wm_e, li_e, g_e,
+                                                                                ring, te);
 }
 
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false,
-          bool A8 = false>
+          bool A8 = false, bool T16 = false>
 static hipError_t launch_pf_kernel(const DualArgs &a, hipStream_t stream) {
     const int64_t tiles_n = (a.n + BN - 1) / BN, tiles_m = (a.b + BM - 1) / BM;
-    hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, STORE_ACC, LR4, GRP, A8>), dim3((unsigned)(tiles_n * tiles_m)),
+    hipLaunchKernelGGL((dual_linear_pf<BN, BM, WN, WM, S, GM, RB, STORE_ACC, LR4, GRP, A8, T16>), dim3((unsigned)(tiles_n * tiles_m)),
                        dim3(WN * WM * 64), 0, stream, a, (int)tiles_n, (int)tiles_m);
     return hipGetLastError();
 }
@@ -967,8 +1062,13 @@ static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
     if (a.acc)
         return four ? launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, true>(a, stream)
                     : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, true>(a, stream);
-    if (a.group) return launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, false, true>(a, stream);
+    if (a.group)
+        return a.t16 ? launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, false, true, false, true>(a, stream)
+                     : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, false, true>(a, stream);
     if (a.lr4) return launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, true>(a, stream);
+    if (a.t16)  // T as fp16: the low-rank operands go through the ring (pf_lowrank_lds)
+        return four ? launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, false, false, false, false, true>(a, stream)
+                    : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, false, false, false, true>(a, stream);
     return four ? launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, false>(a, stream)
                 : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false>(a, stream);
 }

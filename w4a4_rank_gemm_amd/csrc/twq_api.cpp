@@ -167,6 +167,11 @@ int linear_run(const void *x, const void *qw, const float *sw, const void *l1t, 
     act.keep_partials = L.direct;
     act.group = group;
     act.a8 = a8;
+    // many-token fused launch with T reduced from slices: T is stored as fp16 (in the fp32
+    // T's space), which the launch's epilogue streams through its LDS ring
+    int dfn, dfm;
+    const bool t16 = r > 0 && L.plan.ks > 1 && !L.direct && !twq::decode_shape(b, m, n, dfn, dfm) && !a8;
+    act.t16 = t16 ? reinterpret_cast<uint16_t *>(ws + L.t) : nullptr;
     hipError_t e = main_only ? hipSuccess : twq::launch_act(act, L.plan, st);
     if (e != hipSuccess) return hip_fail(e, name);
 
@@ -187,6 +192,7 @@ int linear_run(const void *x, const void *qw, const float *sw, const void *l1t, 
     a.n = n;
     a.group = group;
     a.a8 = a8;
+    a.t16 = act.t16;
     e = twq::launch_dual_linear(a, st);
     return e == hipSuccess ? TWQ_OK : hip_fail(e, name);
 }

@@ -40,6 +40,8 @@ struct ActArgs {
     int group;          // 0: one scale per token row, s_X [b]; kGroup: one scale per kGroup
                         // consecutive elements of a row, s_X group-major [m / kGroup][b]
     int a8;             // 8-bit activations (q_max = 127): qx holds one int8 code per element [b][m]
+    uint16_t *t16;      // ks > 1: the reduction writes T here as fp16 [b][r] (rounded to nearest
+                        // even, as the fused epilogue rounds T) instead of fp32 T; else NULL
 };
 
 // Group size of the group-wise variant: one K stage of every main loop.
@@ -88,6 +90,7 @@ struct DualArgs {
     const uint8_t *ql2;// [n][r/2] packed Q_L2
     int group;         // kGroup: group-wise scales, sx [m / kGroup][b] and sw [m / kGroup][n]
     int a8;            // 8-bit activation codes: qx int8 [b][m] (W4A8)
+    const uint16_t *t16;  // many-token kernels: T already rounded to fp16 [b][r], or NULL (fp32 t)
 };
 
 hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream);
