@@ -633,7 +633,7 @@ __device__ __forceinline__ void pf_store(const DualArgs &a, const v4f (&y)[FN][F
 // fp16, a.t16). A step of 32 ranks needs the tile's BN rows of L2^T and BM rows of T,
 // 64 bytes each: the shape of one main-loop stage, so it is loaded, laid out and read
 // exactly as one (direct-to-LDS loads, two slots, the next step in flight while this one
-// is used), and no register holds a load in flight. Measured on MI355X at b = m = 8192,
+// is used, one barrier a step), and no register holds a load in flight. Measured on MI355X at b = m = 8192,
 // n = 28672, r = 128: this branch cost 98 us of the 1306 us kernel with its operands
 // loaded into registers step by step (four round trips per tile); the ring hides all but
 // the first. The buffers' record counts are the operands' exact sizes, so the half step
@@ -682,13 +682,15 @@ __device__ __forceinline__ void pf_lowrank_lds(const DualArgs &a, v4f (&y)[FN][F
     wait_vmcnt<0>();
     stage_barrier();  // every wave is done with the main loop's last stage
     issue(0, std::integral_constant<int, 0>{});
-    issue(1, std::integral_constant<int, 1>{});
+    // step st: wait until it has landed, meet (which also certifies that every wave is done
+    // with step st - 1's slot), refill that slot with step st + 1, then use step st
     for (int s0 = 0; s0 < nst; s0 += 2) {
         static_for(std::make_integer_sequence<int, 2>{}, [&](auto u) {
             const int st = s0 + u;
             if (st >= nst) return;
-            wait_vmcnt<DPT>();  // step st landed for this thread (step st + 1 may be in flight)
-            stage_barrier();    // ... and for every thread
+            wait_vmcnt<0>();  // step st landed for this thread
+            stage_barrier();  // ... and for every thread; step st - 1's slot is free
+            issue(st + 1, std::integral_constant<int, 1 - decltype(u)::value>{});
             v4i raw[8];
             lds_read_4x4<decltype(u)::value * SLOT, BLK>(rda, rdb, raw);
             const bool live = st * 32 + g * 8 < a.r;  // r is a multiple of 16
@@ -698,8 +700,6 @@ __device__ __forceinline__ void pf_lowrank_lds(const DualArgs &a, v4f (&y)[FN][F
                 for (int fm = 0; fm < FM; ++fm)
                     y[fn][fm] = mfma_f16(__builtin_bit_cast(v8h, raw[fn]), live ? __builtin_bit_cast(v8h, raw[4 + fm]) : v8h{},
                                          y[fn][fm]);
-            stage_barrier();  // every wave is done with this slot
-            issue(st + 2, u);
         });
     }
     wait_vmcnt<0>();  // no load may still be writing this CTA's LDS when it ends
