@@ -183,7 +183,9 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
 // flight). Written as one statement because the compiler cannot tell these reads
 // apart from the direct-to-LDS loads still in flight into other ring slots, and would
 // otherwise wait for all of those first. The offsets ride in the instructions'
-// 16-bit immediate field.
+// 16-bit immediate field. The outputs are early-clobber ("=&v"): a read can return
+// while later reads of the statement are still to issue, so no output may share a
+// register with an address (the compiler otherwise may, where the address dies here).
 template <int OFF, int BLK>
 __device__ __forceinline__ void lds_read_4x4(uint32_t a, uint32_t b, v4i (&r)[8]) {
     static_assert(OFF >= 0 && OFF + 3 * BLK < 65536, "ds_read immediate offset");
@@ -197,7 +199,7 @@ __device__ __forceinline__ void lds_read_4x4(uint32_t a, uint32_t b, v4i (&r)[8]
         "ds_read_b128 %6, %9 offset:%12\n\t"
         "ds_read_b128 %7, %9 offset:%13\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7])
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
         : "v"(a), "v"(b), "n"(OFF), "n"(OFF + BLK), "n"(OFF + 2 * BLK), "n"(OFF + 3 * BLK)
         : "memory");
 }
@@ -222,8 +224,8 @@ __device__ __forceinline__ void lds_read_4x4x4(uint32_t a, uint32_t b0, uint32_t
         "ds_read_b128 %10, %14 offset:%17\n\t"
         "ds_read_b128 %11, %14 offset:%18\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
-          "=v"(r[8]), "=v"(r[9]), "=v"(r[10]), "=v"(r[11])
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+          "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
         : "v"(a), "v"(b0), "v"(b1), "n"(OFF), "n"(OFF + BLK), "n"(OFF + 2 * BLK), "n"(OFF + 3 * BLK)
         : "memory");
 }
@@ -250,7 +252,7 @@ __device__ __forceinline__ void lds_read_2(uint32_t a, v4i (&r)[2]) {
         "ds_read_b128 %0, %2 offset:%3\n\t"
         "ds_read_b128 %1, %2 offset:%4\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(r[0]), "=v"(r[1])
+        : "=&v"(r[0]), "=&v"(r[1])
         : "v"(a), "n"(OFF), "n"(OFF + BLK)
         : "memory");
 }
@@ -266,7 +268,7 @@ __device__ __forceinline__ void lds_read_4(uint32_t a, v4i (&r)[4]) {
         "ds_read_b128 %2, %4 offset:%7\n\t"
         "ds_read_b128 %3, %4 offset:%8\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3])
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
         : "v"(a), "n"(OFF), "n"(OFF + BLK), "n"(OFF + 2 * BLK), "n"(OFF + 3 * BLK)
         : "memory");
 }
@@ -289,7 +291,7 @@ __device__ __forceinline__ void lds_read_scales(uint32_t w, uint32_t x, v4f (&sw
         "ds_read_b32 %6, %9 offset:%12\n\t"
         "ds_read_b32 %7, %9 offset:%13\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(sw[0]), "=v"(sw[1]), "=v"(sw[2]), "=v"(sw[3]), "=v"(sx[0]), "=v"(sx[1]), "=v"(sx[2]), "=v"(sx[3])
+        : "=&v"(sw[0]), "=&v"(sw[1]), "=&v"(sw[2]), "=&v"(sw[3]), "=&v"(sx[0]), "=&v"(sx[1]), "=&v"(sx[2]), "=&v"(sx[3])
         : "v"(w), "v"(x), "n"(OFF), "n"(OFF + 64), "n"(OFF + 128), "n"(OFF + 192)
         : "memory");
 }
