@@ -632,88 +632,112 @@ __device__ __forceinline__ void pf_store(const DualArgs &a, const v4f (&y)[FN][F
 // The fp16 low-rank branch with its operands staged through the CTA's LDS ring (T as
 // fp16, a.t16). A step of 32 ranks needs the tile's BN rows of L2^T and BM rows of T,
 // 64 bytes each: the shape of one main-loop stage, so it is loaded, laid out and read
-// exactly as one (direct-to-LDS loads, two slots, the next step in flight while this one
-// is used, one barrier a step), and no register holds a load in flight. Measured on MI355X at b = m = 8192,
-// n = 28672, r = 128: this branch cost 98 us of the 1306 us kernel with its operands
-// loaded into registers step by step (four round trips per tile); the ring hides all but
-// the first. The buffers' record counts are the operands' exact sizes, so the half step
-// past r (r an odd multiple of 16) of the last row reads zeros; other rows' dead ranks are
-// zeroed below, as in the register path. The sums are the register path's, in the same
+// exactly as one (direct-to-LDS loads, no register holds a load in flight), and the steps
+// continue the main loop's ring: its last S - 1 steps load low-rank steps 0 .. S - 2 into
+// the slots they free, and the epilogue keeps S steps in flight. Measured on MI355X at
+// b = m = 8192, n = 28672, r = 128: this branch cost 98 us of the 1306 us kernel with its
+// operands loaded into registers step by step (each step a round trip to memory); its
+// loads barely overlap the few MFMAs a step takes, so the round trips, not the slots,
+// are what to save. The buffers' record counts are the operands' exact sizes, so the half
+// step past r (r an odd multiple of 16) of the last row reads zeros; other rows' dead ranks
+// are zeroed below, as in the register path. The sums are the register path's, in the same
 // order, on the same fp16 values: Y is the same bit for bit.
-template <int BN, int BM, int WN, int WM, int SLOT, int FN, int FM>
-__device__ __forceinline__ void pf_lowrank_lds(const DualArgs &a, v4f (&y)[FN][FM], int64_t ch0, int64_t tok0, int wn,
-                                               int wm, int li, int g, uint8_t *ring, int tid) {
-    constexpr int NT = WN * WM * 64, CPR = 4, BLK = 1024, ROWS = BN + BM, DPT = ROWS * CPR / NT;
-    static_assert(ROWS * 64 <= SLOT && (BN * CPR) % NT == 0 && FN == 4 && FM == 4, "one step fits a ring slot");
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int nst = (a.r + 31) / 32;
-    // this thread's loads of a step: the main loop's (row, 16-byte chunk) mapping, rows of
-    // L2^T (channel rows, first BN) or of T (token rows), clamped into the operand
-    uint32_t off[DPT];
-#pragma unroll
-    for (int j = 0; j < DPT; ++j) {
-        const int q = j * NT + tid;
-        const int line = (q % 64) / 8, logical = (q % 8) ^ line;
-        const int row = (q / 64) * 16 + 2 * line + logical / 4, chunk = logical % 4;
-        const int64_t rr = row < BN ? (ch0 + row < a.n ? ch0 + row : a.n - 1)
-                                    : (tok0 + row - BN < a.b ? tok0 + row - BN : a.b - 1);
-        off[j] = (uint32_t)(rr * a.r * 2 + chunk * 16);
-    }
+
+// Low-rank step e (past the last: the last again) of the tile at (ch0, tok0) into ring slot
+// `slot`: the main loop's (row, 16-byte chunk) mapping, rows of L2^T (channel rows, first
+// BN) or of T (token rows), clamped into the operand. XS: the stages carry group scales,
+// and one more 4-byte load lands in the slot's scale area (never read), so a step issues
+// as many loads as a stage. The offsets are formed here from a copy of the thread index the
+// compiler cannot see through, so they are not kept live across the main loop.
+template <int BN, int BM, int NT, int SLOT, int XS>
+__device__ __forceinline__ void pf_lr_issue(const DualArgs &a, int64_t ch0, int64_t tok0, uint8_t *ring, int slot, int e,
+                                            int tid) {
+    constexpr int CPR = 4, DPT = (BN + BM) * CPR / NT;
+    static_assert((BN * CPR) % NT == 0 && NT % kWave == 0, "each load group in one operand");
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int last = (a.r + 31) / 32 - 1;
+    const int sc = e < last ? e : last;
     const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.l2t), 0,
                                                                         (int)(a.n * a.r * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.t16), 0,
                                                                         (int)(a.b * a.r * 2), 0x00020000);
-    auto issue = [&](int st, auto slot) {
-        uint8_t *dst = ring + decltype(slot)::value * SLOT;
-        const int sc = st < nst ? st : nst - 1;  // past the last step: reloaded, unused
+    uint8_t *dst = ring + slot * SLOT;
+    // lane l of load j: row 16 (4 j + wave) + 2 (l / 8) + c / 4 of the step, 16-byte chunk
+    // c % 4, c = (l % 8) ^ (l / 8); indices fit 32 bits (n r and b r do)
+    const int lane = t % kWave, line = lane / 8, logical = (lane % 8) ^ line;
+    const int lrow = 2 * line + logical / 4, lchunk = (logical % 4) * 16;
+    const int nlast = (int)a.n - 1, blast = (int)a.b - 1, r2 = a.r * 2;
 #pragma unroll
-        for (int j = 0; j < DPT; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds((j * NT) / CPR < BN ? rl : rt,
-                                                     (__attribute__((address_space(3))) void *)(dst + (j * NT + wave * kWave) * 16),
-                                                     16, (int)off[j], sc * 64, 0, 0);
-    };
+    for (int j = 0; j < DPT; ++j) {
+        const int row = (j * (NT / kWave) + wave) * 16 + lrow;  // j * NT / CPR rows before load j
+        const int rr = (j * NT) / CPR < BN ? ((int)ch0 + row < nlast ? (int)ch0 + row : nlast)
+                                           : ((int)tok0 + row - BN < blast ? (int)tok0 + row - BN : blast);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((j * NT) / CPR < BN ? rl : rt,
+                                                 (__attribute__((address_space(3))) void *)(dst + (j * NT + wave * kWave) * 16),
+                                                 16, rr * r2 + lchunk, sc * 64, 0, 0);
+    }
+    if constexpr (XS > 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void *)(dst + XS + wave * kWave * 4), 4,
+                                                 0, 0, 0, 0);
+}
+
+// The low-rank steps after the main loop. nst: main-loop stages; low-rank step e sits in
+// slot (nst + e) % S; steps 0 .. S - 2 were issued by the main loop's last steps (LPT
+// loads each, as a stage). Step e: wait until it has landed (the later steps still in
+// flight), meet, use it, and, if a step is still to load, meet again (every wave is done
+// with the slot) and load step e + S into it. Two barriers a step instead of one, but S
+// steps in flight instead of S - 1: the MFMAs between them are few.
+template <int BN, int BM, int WN, int WM, int S, int SLOT, int LPT, int XS, int FN, int FM>
+__device__ __forceinline__ void pf_lowrank_ring(const DualArgs &a, v4f (&y)[FN][FM], int64_t ch0, int64_t tok0, int wn,
+                                                int wm, int li, int g, uint8_t *ring, int tid, int nst) {
+    constexpr int NT = WN * WM * 64, BLK = 1024;
+    static_assert((BN + BM) * 64 <= SLOT && FN == 4 && FM == 4 && S >= 2 && S <= 3, "one step fits a ring slot");
+    const int nlr = (a.r + 31) / 32;
     // operand reads: row li, chunk g of a block, as in the main loop
     const uint32_t lane_off = (li / 2) * 128 + ((4 * (li % 2) + g) ^ (li / 2)) * 16;
     const uint32_t rda = lds_offset(ring) + lane_off + (wn * (BN / WN) / 16) * BLK;
     const uint32_t rdb = lds_offset(ring) + lane_off + ((BN + wm * (BM / WM)) / 16) * BLK;
 
-    // the main loop's look-ahead loads (its last steps reload the last stage into slots no
-    // step reads) must have landed before these slots are refilled: drain them, then meet
-    wait_vmcnt<0>();
-    stage_barrier();  // every wave is done with the main loop's last stage
-    issue(0, std::integral_constant<int, 0>{});
-    // step st: wait until it has landed, meet (which also certifies that every wave is done
-    // with step st - 1's slot), refill that slot with step st + 1, then use step st
-    for (int s0 = 0; s0 < nst; s0 += 2) {
-        static_for(std::make_integer_sequence<int, 2>{}, [&](auto u) {
-            const int st = s0 + u;
-            if (st >= nst) return;
-            wait_vmcnt<0>();  // step st landed for this thread
-            stage_barrier();  // ... and for every thread; step st - 1's slot is free
-            issue(st + 1, std::integral_constant<int, 1 - decltype(u)::value>{});
-            v4i raw[8];
-            lds_read_4x4<decltype(u)::value * SLOT, BLK>(rda, rdb, raw);
-            const bool live = st * 32 + g * 8 < a.r;  // r is a multiple of 16
+    int slot = nst % S;  // step 0's
+    stage_barrier();     // every wave is done with the main loop's last stage, in slot (nst + S - 1) % S
+    if (S - 1 < nlr) pf_lr_issue<BN, BM, NT, SLOT, XS>(a, ch0, tok0, ring, slot == 0 ? S - 1 : slot - 1, S - 1, tid);
+    for (int e = 0; e < nlr; ++e) {
+        // loads issued after step e's: those of the next steps (if fewer, waiting for more is safe)
+        const int ahead = nlr - 1 - e;
+        if (S > 2 && ahead >= 2)
+            wait_vmcnt<(S > 2 ? 2 : 1) * LPT>();
+        else if (ahead >= 1)
+            wait_vmcnt<LPT>();
+        else
+            wait_vmcnt<0>();
+        stage_barrier();  // step e landed for every thread
+        v4i raw[8];
+        lds_read_4x4<0, BLK>(rda + slot * SLOT, rdb + slot * SLOT, raw);
+        const bool live = e * 32 + g * 8 < a.r;  // r is a multiple of 16
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+        for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-                    y[fn][fm] = mfma_f16(__builtin_bit_cast(v8h, raw[fn]), live ? __builtin_bit_cast(v8h, raw[4 + fm]) : v8h{},
-                                         y[fn][fm]);
-        });
+            for (int fm = 0; fm < FM; ++fm)
+                y[fn][fm] = mfma_f16(__builtin_bit_cast(v8h, raw[fn]), live ? __builtin_bit_cast(v8h, raw[4 + fm]) : v8h{},
+                                     y[fn][fm]);
+        if (e + S < nlr) {
+            stage_barrier();  // every wave is done with this slot
+            pf_lr_issue<BN, BM, NT, SLOT, XS>(a, ch0, tok0, ring, slot, e + S, tid);
+        }
+        slot = slot + 1 == S ? 0 : slot + 1;
     }
     wait_vmcnt<0>();  // no load may still be writing this CTA's LDS when it ends
 }
 
 // Second half of the many-token epilogue, from the dequantized residual y of a wave's
 // FN x FM tiles of 16 x 16 (the wave at (wn, wm) of a BN x BM CTA tile at (ch0, tok0)):
-// add the low-rank branch and store fp16.
-// SLOT > 0: T comes as fp16 (a.t16), and the CTA's LDS ring (two slots of SLOT bytes, free
-// once the main loop is done) carries the low-rank operands, see pf_lowrank_lds. A
-// compile-time choice: with both paths in one kernel the four-CTA kernel spilled.
-template <int BN, int BM, int WN, int WM, bool LR4, int SLOT, int FN, int FM>
+// add the low-rank branch and store fp16 (T as fp32, operands loaded into registers; with
+// T as fp16 the kernel takes pf_lowrank_ring instead).
+template <int BN, int BM, int WN, int WM, bool LR4, int FN, int FM>
 __device__ __forceinline__ void pf_finish(const DualArgs &a, v4f (&y)[FN][FM], int64_t ch0, int64_t tok0, int wn, int wm,
-                                          int li, int g, uint8_t *ring, int tid) {
+                                          int li, int g) {
     if constexpr (LR4) {
         // int4 low-rank branch: y += s_H (Q_H Q_L2^T)
         if (a.r > 0) {
@@ -733,13 +757,6 @@ __device__ __forceinline__ void pf_finish(const DualArgs &a, v4f (&y)[FN][FM], i
     // fp16 low-rank branch: y += L2^T (channels x ranks) . T^T (ranks x tokens). Rows are
     // addressed by 32-bit element offsets from the uniform bases (n r and b r stay below
     // 2^32 within the ABI's limits) rather than one 64-bit pointer per row.
-    if constexpr (SLOT > 0 && !LR4) {
-        if (a.r > 0) {
-            pf_lowrank_lds<BN, BM, WN, WM, SLOT>(a, y, ch0, tok0, wn, wm, li, g, ring, tid);
-            pf_store<BN, BM, WN, WM>(a, y, ch0, tok0, wn, wm, li, g);
-            return;
-        }
-    }
     const int64_t chb = ch0 + wn * (BN / WN) + li, tkb = tok0 + wm * (BM / WM) + li;
     for (int k0 = 0; k0 < (LR4 ? 0 : a.r); k0 += 32) {
         const int rank = k0 + g * 8;
@@ -768,9 +785,9 @@ __device__ __forceinline__ void pf_finish(const DualArgs &a, v4f (&y)[FN][FM], i
 // Epilogue of the many-token kernels: dequantize the integer sums, then pf_finish (or
 // store the exact integer sums). SH: log2 of the operands' combined scale in acc (8 for
 // 4-bit x 4-bit, 4 for W4A8).
-template <int BN, int BM, int WN, int WM, bool STORE_ACC, bool LR4, int SH, int SLOT, int FN, int FM>
+template <int BN, int BM, int WN, int WM, bool STORE_ACC, bool LR4, int SH, int FN, int FM>
 __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM], int64_t ch0, int64_t tok0, int wn, int wm,
-                                            int li, int g, uint8_t *ring, int tid) {
+                                            int li, int g) {
     // lane (li, g), register v of tile (fn, fm) holds channel ch_base + 4g + v, token tok_base + li
     if constexpr (STORE_ACC) {
 #pragma unroll
@@ -799,7 +816,7 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 #pragma unroll
                 for (int v = 0; v < 4; ++v) y[fn][fm][v] = (sxv[fm] * swv[v]) * (float)(acc[fn][fm][v] >> SH);
         }
-        pf_finish<BN, BM, WN, WM, LR4, SLOT>(a, y, ch0, tok0, wn, wm, li, g, ring, tid);
+        pf_finish<BN, BM, WN, WM, LR4>(a, y, ch0, tok0, wn, wm, li, g);
     }
 }
 
@@ -809,8 +826,9 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 // accumulators). W4A8's stages are 24 KB, so it runs a two-stage ring (one stage in
 // flight) to fit three CTAs per unit: 2-10% faster than three stages at two CTAs.
 // The per-token W4A4 kernel on a two-stage ring fits four CTAs per unit (128 registers,
-// a few spilled around the epilogue only); launch_pf takes it where the grid fills all
-// four slots of every unit at least once (see there).
+// none spilled: the loads' LDS destinations are uniform, formed from the wave index in
+// a scalar register); launch_pf takes it where the grid fills all four slots of every
+// unit at least once (see there).
 //
 // GRP (groups of kGroup = 128 along K): a stage is one group. Each slot of the ring
 // also holds the stage's scales, s_W of the tile's BN channels and s_X of its BM tokens
@@ -894,7 +912,11 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
         off[j] = (uint32_t)(row < BN ? qw_offset(rel, chunk * 16, a.m)
                                      : rel * xb + (A8 ? chunk * 32 + ((row - BN) / BM) * 16 : chunk * 16));
     }
-    __shared__ __attribute__((aligned(16))) uint8_t ring[S * SLOT];
+    // T16 (per-token scales): s_W of the tile's BN channels, then s_X of its BM tokens, past
+    // the ring, loaded before the main loop (one 4-byte load a thread), so the epilogue
+    // reads them from LDS instead of waiting for them
+    constexpr int SCL = T16 && !GRP ? 4 * (BN + BM) : 0;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[S * SLOT + SCL];
     // GRP: this thread's scale: waves 0-1 load s_W of channel ch0 + tid, waves 2-3 s_X of
     // token tok0 + tid - 128 (rows past n or b clamped), into the slot's scale area
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -910,11 +932,17 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wbase), 0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xbase), 0, 0x7fffffff, 0x00020000);
     auto issue = [&](int st, auto slot) {
+        if constexpr (T16) {
+            if (st >= nst) {  // past the last stage: the low-rank steps, into the slots it frees
+                pf_lr_issue<BN, BM, NT, SLOT, GRP ? STAGE_BYTES : 0>(a, ch0, tok0, ring, decltype(slot)::value, st - nst, tid);
+                return;
+            }
+        }
         uint8_t *dst = ring + decltype(slot)::value * SLOT;
 #pragma unroll
         for (int j = 0; j < DPT; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds((j * NT) / CPR < BN ? rw : rx,
-                                                     (__attribute__((address_space(3))) void *)(dst + (j * NT + wave * kWave) * 16),
+                                                     (__attribute__((address_space(3))) void *)(dst + (j * NT + wave_u * kWave) * 16),
                                                      16, (int)off[j], st * RB * ((j * NT) / CPR < BN ? kPanelRows : XH), 0, 0);
         if constexpr (GRP) {
             // group st's row of the group-major scales, from the tile's first channel or token
@@ -962,11 +990,22 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
                  ((BN + e * BM + wm * (BM / WM)) / 16) * BLK;
     }
 
+    if constexpr (SCL > 0) {
+        // waves 0 .. BN/64 - 1: s_W of channel ch0 + tid, the others s_X of token
+        // tok0 + tid - BN (rows past n or b clamped); the first wait below covers it
+        static_assert(BN + BM == NT, "one scale a thread");
+        const bool wv = wave_u < BN / kWave;
+        const int64_t idx = wv ? (ch0 + tid < a.n ? ch0 + tid : a.n - 1) : (tok0 + tid - BN < a.b ? tok0 + tid - BN : a.b - 1);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(wv ? a.sw : a.sx), 0,
+                                                                            (int)((wv ? a.n : a.b) * 4), 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(ring + S * SLOT + wave_u * kWave * 4),
+                                                 4, (int)(idx * 4), 0, 0, 0);
+    }
     // Step st issues stage st into slot st % S and consumes stage st - (S - 1). Every
     // step issues (past the last stage it loads the last stage again, into a slot no
-    // later step reads), so the count of loads in flight is the same at every wait and
-    // the compiler sees no branch around a load. The loop is unrolled by the ring
-    // depth, so every slot is a compile-time constant.
+    // later step reads, or with T16 the first low-rank steps), so the count of loads in
+    // flight is the same at every wait and the compiler sees no branch around a load.
+    // The loop is unrolled by the ring depth, so every slot is a compile-time constant.
     for (int s0 = 0; s0 < nst + S - 1; s0 += S) {
         static_for(std::make_integer_sequence<int, S>{}, [&](auto u) {
             const int st = s0 + u, c = st - (S - 1);
@@ -975,7 +1014,7 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
                 wait_vmcnt<(S - 2) * LPT>();
                 stage_barrier();  // stage c landed for every thread; stage c - 1 consumed by every wave
             }
-            issue(st < nst ? st : nst - 1, u);
+            issue(T16 || st < nst ? st : nst - 1, u);
             if (c < 0) return;
             constexpr int OFF = ((u + 1) % S) * SLOT;  // slot of stage c
             v4f swr[4];
@@ -1029,11 +1068,31 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     asm volatile("" : "+v"(te));
     const int li_e = te & 15, g_e = (te >> 4) & 3;
     const int wn_e = wave_u % WN, wm_e = wave_u / WN;
-    if constexpr (GRP)
-        pf_finish<BN, BM, WN, WM, false, T16 ? SLOT : 0>(a, yg, ch0, tok0, wn_e, wm_e, li_e, g_e, ring, te);
-    else
-        pf_epilogue<BN, BM, WN, WM, STORE_ACC, LR4, A8 ? 4 : 8, T16 ? SLOT : 0>(a, acc, ch0, tok0, wn_e, wm_e, li_e, g_e,
-                                                                                ring, te);
+    if constexpr (T16) {
+        if constexpr (GRP) {
+            pf_lowrank_ring<BN, BM, WN, WM, S, SLOT, LPT, STAGE_BYTES>(a, yg, ch0, tok0, wn_e, wm_e, li_e, g_e, ring, te, nst);
+            pf_store<BN, BM, WN, WM>(a, yg, ch0, tok0, wn_e, wm_e, li_e, g_e);
+        } else {
+            // dequantize with the scales from LDS, as pf_epilogue does with them from memory
+            v4f swr[FN];
+            float sxr[FM];
+            lds_read_scales<S * SLOT>(lds_offset(ring) + (wn_e * (BN / WN) + 4 * g_e) * 4,
+                                      lds_offset(ring) + (BN + wm_e * (BM / WM) + li_e) * 4, swr, sxr);
+            v4f y[FN][FM];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) y[fn][fm][v] = (sxr[fm] * swr[fn][v]) * (float)(acc[fn][fm][v] >> 8);
+            pf_lowrank_ring<BN, BM, WN, WM, S, SLOT, LPT, 0>(a, y, ch0, tok0, wn_e, wm_e, li_e, g_e, ring, te, nst);
+            pf_store<BN, BM, WN, WM>(a, y, ch0, tok0, wn_e, wm_e, li_e, g_e);
+        }
+    } else if constexpr (GRP) {
+        pf_finish<BN, BM, WN, WM, false>(a, yg, ch0, tok0, wn_e, wm_e, li_e, g_e);
+    } else {
+        pf_epilogue<BN, BM, WN, WM, STORE_ACC, LR4, A8 ? 4 : 8>(a, acc, ch0, tok0, wn_e, wm_e, li_e, g_e);
+    }
 }
 
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false,
@@ -1066,7 +1125,7 @@ static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
         return a.t16 ? launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, false, true, false, true>(a, stream)
                      : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, false, true>(a, stream);
     if (a.lr4) return launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, true>(a, stream);
-    if (a.t16)  // T as fp16: the low-rank operands go through the ring (pf_lowrank_lds)
+    if (a.t16)  // T as fp16: the low-rank operands go through the ring (pf_lowrank_ring)
         return four ? launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, false, false, false, false, true>(a, stream)
                     : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, false, false, false, true>(a, stream);
     return four ? launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, false>(a, stream)
