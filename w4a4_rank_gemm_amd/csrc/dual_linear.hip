@@ -649,7 +649,7 @@ __device__ __forceinline__ void pf_store(const DualArgs &a, const v4f (&y)[FN][F
 // and one more 4-byte load lands in the slot's scale area (never read), so a step issues
 // as many loads as a stage. The offsets are formed here from a copy of the thread index the
 // compiler cannot see through, so they are not kept live across the main loop.
-template <int BN, int BM, int NT, int SLOT, int XS>
+template <int BN, int BM, int NT, int SLOT, int XS, bool ODD = false>
 __device__ __forceinline__ void pf_lr_issue(const DualArgs &a, int64_t ch0, int64_t tok0, uint8_t *ring, int slot, int e,
                                             int tid) {
     constexpr int CPR = 4, DPT = (BN + BM) * CPR / NT;
@@ -666,7 +666,9 @@ __device__ __forceinline__ void pf_lr_issue(const DualArgs &a, int64_t ch0, int6
     uint8_t *dst = ring + slot * SLOT;
     // lane l of load j: row 16 (4 j + wave) + 2 (l / 8) + c / 4 of the step, 16-byte chunk
     // c % 4, c = (l % 8) ^ (l / 8); indices fit 32 bits (n r and b r do)
-    const int lane = t % kWave, line = lane / 8, logical = (lane % 8) ^ line;
+    // ODD (the 32 x 32 kernel's layout): odd 1 KB blocks -- each wave fills one -- have
+    // bit 0 of the chunk position flipped as well
+    const int lane = t % kWave, line = lane / 8, logical = (lane % 8) ^ line ^ (ODD ? (wave & 1) : 0);
     const int lrow = 2 * line + logical / 4, lchunk = (logical % 4) * 16;
     const int nlast = (int)a.n - 1, blast = (int)a.b - 1, r2 = a.r * 2;
 #pragma unroll
@@ -825,10 +827,8 @@ __device__ __forceinline__ void pf_epilogue(const DualArgs &a, v4i (&acc)[FN][FM
 // shapes, the group-wise variant (GRP) included, which keeps a second, fp32 set of
 // accumulators). W4A8's stages are 24 KB, so it runs a two-stage ring (one stage in
 // flight) to fit three CTAs per unit: 2-10% faster than three stages at two CTAs.
-// The per-token W4A4 kernel on a two-stage ring fits four CTAs per unit (128 registers,
-// none spilled: the loads' LDS destinations are uniform, formed from the wave index in
-// a scalar register); launch_pf takes it where the grid fills all four slots of every
-// unit at least once (see there).
+// (The per-token 4-bit layer runs dual_linear_pf32 below, which keeps this kernel's ring
+// and tile order on 32 x 32 matrix blocks.)
 //
 // GRP (groups of kGroup = 128 along K): a stage is one group. Each slot of the ring
 // also holds the stage's scales, s_W of the tile's BN channels and s_X of its BM tokens
@@ -865,7 +865,8 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     static_assert(!GRP || (RB == 64 && BN == 128 && BM == 128 && NT == 256 && !STORE_ACC && !LR4),
                   "group-wise: one group per stage, one scale load per thread");
 
-    static_assert(!T16 || (!A8 && !LR4 && !STORE_ACC && RB == 64), "fp16 T through the ring: 64-byte stages");
+    static_assert(!T16 || (GRP && !A8 && !LR4 && !STORE_ACC && RB == 64),
+                  "fp16 T through the ring: group-wise, 64-byte stages (per-token: dual_linear_pf32)");
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int li = lane & 15, g = lane >> 4;
     const int wn = wave % WN, wm = wave / WN;
@@ -912,11 +913,7 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
         off[j] = (uint32_t)(row < BN ? qw_offset(rel, chunk * 16, a.m)
                                      : rel * xb + (A8 ? chunk * 32 + ((row - BN) / BM) * 16 : chunk * 16));
     }
-    // T16 (per-token scales): s_W of the tile's BN channels, then s_X of its BM tokens, past
-    // the ring, loaded before the main loop (one 4-byte load a thread), so the epilogue
-    // reads them from LDS instead of waiting for them
-    constexpr int SCL = T16 && !GRP ? 4 * (BN + BM) : 0;
-    __shared__ __attribute__((aligned(16))) uint8_t ring[S * SLOT + SCL];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[S * SLOT];
     // GRP: this thread's scale: waves 0-1 load s_W of channel ch0 + tid, waves 2-3 s_X of
     // token tok0 + tid - 128 (rows past n or b clamped), into the slot's scale area
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -990,17 +987,6 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
                  ((BN + e * BM + wm * (BM / WM)) / 16) * BLK;
     }
 
-    if constexpr (SCL > 0) {
-        // waves 0 .. BN/64 - 1: s_W of channel ch0 + tid, the others s_X of token
-        // tok0 + tid - BN (rows past n or b clamped); the first wait below covers it
-        static_assert(BN + BM == NT, "one scale a thread");
-        const bool wv = wave_u < BN / kWave;
-        const int64_t idx = wv ? (ch0 + tid < a.n ? ch0 + tid : a.n - 1) : (tok0 + tid - BN < a.b ? tok0 + tid - BN : a.b - 1);
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(wv ? a.sw : a.sx), 0,
-                                                                            (int)((wv ? a.n : a.b) * 4), 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(ring + S * SLOT + wave_u * kWave * 4),
-                                                 4, (int)(idx * 4), 0, 0, 0);
-    }
     // Step st issues stage st into slot st % S and consumes stage st - (S - 1). Every
     // step issues (past the last stage it loads the last stage again, into a slot no
     // later step reads, or with T16 the first low-rank steps), so the count of loads in
@@ -1068,31 +1054,318 @@ void dual_linear_pf(DualArgs a, int tiles_n, int tiles_m) {
     asm volatile("" : "+v"(te));
     const int li_e = te & 15, g_e = (te >> 4) & 3;
     const int wn_e = wave_u % WN, wm_e = wave_u / WN;
-    if constexpr (T16) {
-        if constexpr (GRP) {
-            pf_lowrank_ring<BN, BM, WN, WM, S, SLOT, LPT, STAGE_BYTES>(a, yg, ch0, tok0, wn_e, wm_e, li_e, g_e, ring, te, nst);
-            pf_store<BN, BM, WN, WM>(a, yg, ch0, tok0, wn_e, wm_e, li_e, g_e);
-        } else {
-            // dequantize with the scales from LDS, as pf_epilogue does with them from memory
-            v4f swr[FN];
-            float sxr[FM];
-            lds_read_scales<S * SLOT>(lds_offset(ring) + (wn_e * (BN / WN) + 4 * g_e) * 4,
-                                      lds_offset(ring) + (BN + wm_e * (BM / WM) + li_e) * 4, swr, sxr);
-            v4f y[FN][FM];
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) y[fn][fm][v] = (sxr[fm] * swr[fn][v]) * (float)(acc[fn][fm][v] >> 8);
-            pf_lowrank_ring<BN, BM, WN, WM, S, SLOT, LPT, 0>(a, y, ch0, tok0, wn_e, wm_e, li_e, g_e, ring, te, nst);
-            pf_store<BN, BM, WN, WM>(a, y, ch0, tok0, wn_e, wm_e, li_e, g_e);
-        }
+    if constexpr (T16) {  // group-wise (static_assert above)
+        pf_lowrank_ring<BN, BM, WN, WM, S, SLOT, LPT, STAGE_BYTES>(a, yg, ch0, tok0, wn_e, wm_e, li_e, g_e, ring, te, nst);
+        pf_store<BN, BM, WN, WM>(a, yg, ch0, tok0, wn_e, wm_e, li_e, g_e);
     } else if constexpr (GRP) {
         pf_finish<BN, BM, WN, WM, false>(a, yg, ch0, tok0, wn_e, wm_e, li_e, g_e);
     } else {
         pf_epilogue<BN, BM, WN, WM, STORE_ACC, LR4, A8 ? 4 : 8>(a, acc, ch0, tok0, wn_e, wm_e, li_e, g_e);
     }
+}
+
+// ---------------------------------------------------------------------------------
+// Many tokens, per-token scales, 4-bit activations (the one-call layer, the split call
+// with T in fp32, r = 0, and the exact accumulator export): the ring, stages and tile
+// order of dual_linear_pf, with each wave's 64 x 64 tile as 2 x 2 blocks of 32 x 32 on
+// v_mfma_i32_32x32x32_i8 instead of 4 x 4 blocks of 16 x 16. The operand bytes, the
+// expansion work and the matrix-core time per stage are the same; the matrix
+// instructions are half as many, and the issue slots they free go to the expansion
+// beside them, which is what bounds the loop.
+// Lane l reads row l % 32 of a 32-row block (two 16-row LDS blocks), the 16 bytes of
+// chunk 2 h + l / 32 for the stage's halves h = 0, 1, with the same (row, chunk) -> LDS
+// address map as dual_linear_pf, so the reads stay free of bank conflicts. Both operands
+// take the same chunks and expand them the same way, so their codes pair one for one
+// whatever order the instruction sums them in. In the result, lane l holds token l % 32
+// of its block and register v channel 8 (v / 4) + 4 (l / 32) + v % 4.
+//
+// The fp16 low-rank branch runs on v_mfma_f32_32x32x16_f16 with the dequantized sums
+// as its C operand: T16, its operands through the ring (as pf_lowrank_ring); else T in
+// fp32 and L2^T from memory into registers (as pf_finish). Either way each lane takes
+// the 8 ranks of chunk 2 k + l / 32 of a 32-rank step (k = 0, 1) for its row.
+
+// Y of a wave's 2 x 2 blocks of 32 x 32 at (chw, tkw), stored fp16 (rows past n or b
+// not stored; n is a multiple of 16, so a live channel quad is whole).
+__device__ __forceinline__ void pf32_store(const DualArgs &a, const v16f (&y)[2][2], int64_t chw, int64_t tkw, int r32,
+                                           int kh) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t ch = chw + rb * 32 + 8 * q + 4 * kh;
+                const int64_t tok = tkw + cb * 32 + r32;
+                if (ch < a.n && tok < a.b) {
+                    v4h o;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) o[v] = (_Float16)y[rb][cb][4 * q + v];
+                    *reinterpret_cast<v4h *>(a.y + tok * a.n + ch) = o;
+                }
+            }
+}
+
+// The low-rank steps after the main loop, through the ring (pf_lowrank_ring's schedule:
+// steps 0 .. S - 2 were issued by the main loop's last steps into the slots they freed;
+// step e sits in slot (nst + e) % S; S steps in flight, two barriers a step).
+template <int S, int SLOT, int LPT>
+__device__ __forceinline__ void pf32_lowrank_ring(const DualArgs &a, v16f (&y)[2][2], int64_t ch0, int64_t tok0,
+                                                  const uint32_t (&rda)[2], const uint32_t (&rdb)[2], int kh,
+                                                  uint8_t *ring, int tid, int nst) {
+    constexpr int BN = 128, BM = 128, NT = 256, STR = 2048;
+    static_assert(S >= 2 && S <= 3, "ring depth");
+    const int nlr = (a.r + 31) / 32;
+    int slot = nst % S;  // step 0's
+    stage_barrier();     // every wave is done with the main loop's last stage
+    if (S - 1 < nlr) pf_lr_issue<BN, BM, NT, SLOT, 0, true>(a, ch0, tok0, ring, slot == 0 ? S - 1 : slot - 1, S - 1, tid);
+    for (int e = 0; e < nlr; ++e) {
+        const int ahead = nlr - 1 - e;
+        if (S > 2 && ahead >= 2)
+            wait_vmcnt<(S > 2 ? 2 : 1) * LPT>();
+        else if (ahead >= 1)
+            wait_vmcnt<LPT>();
+        else
+            wait_vmcnt<0>();
+        stage_barrier();  // step e landed for every thread
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            // the step's k-th 16 ranks: L2^T rows of the wave's two channel blocks, T rows
+            // of its two token blocks (read half a step at a time: registers are short here)
+            v4i raw[4];
+            lds_read_2x2<0, STR>(rda[k] + slot * SLOT, rdb[k] + slot * SLOT, raw);
+            const bool live = e * 32 + (2 * k + kh) * 8 < a.r;  // r is a multiple of 16
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    y[rb][cb] = mfma_f16_32(__builtin_bit_cast(v8h, raw[rb]), live ? __builtin_bit_cast(v8h, raw[2 + cb]) : v8h{},
+                                            y[rb][cb]);
+        }
+        if (e + S < nlr) {
+            stage_barrier();  // every wave is done with this slot
+            pf_lr_issue<BN, BM, NT, SLOT, 0, true>(a, ch0, tok0, ring, slot, e + S, tid);
+        }
+        slot = slot + 1 == S ? 0 : slot + 1;
+    }
+    wait_vmcnt<0>();  // no load may still be writing this CTA's LDS when it ends
+}
+
+// The low-rank branch from memory (T in fp32, rounded to fp16 as it is loaded; L2^T
+// rows fp16), as pf_finish does for 16 x 16 blocks.
+__device__ __forceinline__ void pf32_lowrank_regs(const DualArgs &a, v16f (&y)[2][2], int64_t chw, int64_t tkw, int r32,
+                                                  int kh) {
+    for (int k0 = 0; k0 < a.r; k0 += 16) {
+        const int rank = k0 + kh * 8;
+        const bool live = rank < a.r;  // r is a multiple of 16: live means rank + 8 <= r
+        const uint32_t rk = live ? rank : 0;
+        v8h la[2], tb[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int64_t ch = chw + rb * 32 + r32;
+            la[rb] = load_h8(a.l2t + ((uint32_t)((ch < a.n ? ch : a.n - 1) * a.r) + rk));
+        }
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const int64_t tok = tkw + cb * 32 + r32;
+            const float4 *tp = reinterpret_cast<const float4 *>(a.t + ((uint32_t)((tok < a.b ? tok : a.b - 1) * a.r) + rk));
+            tb[cb] = live ? f32x8_to_h8(tp[0], tp[1]) : v8h{};
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) y[rb][cb] = mfma_f16_32(la[rb], tb[cb], y[rb][cb]);
+    }
+}
+
+template <int S, int GM, bool STORE_ACC, bool T16>
+__global__ __launch_bounds__(256, S == 2 ? 4 : 3) void dual_linear_pf32(DualArgs a, int tiles_n, int tiles_m) {
+    constexpr int BN = 128, BM = 128, WN = 2, WM = 2, RB = 64, NT = 256;
+    constexpr int CPR = RB / 16, BLK = 16 * RB, ROWS = BN + BM, SLOT = ROWS * RB, DPT = ROWS * CPR / NT;
+    static_assert(!(STORE_ACC && T16) && (S - 2) * DPT < 64, "one epilogue; loads in flight fit vmcnt");
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int wn = wave % WN, wm = wave / WN;
+
+    // block -> tile, as in dual_linear_pf
+    const int ntiles = tiles_n * tiles_m;
+    const int o = (int)xcd_order(blockIdx.x, ntiles);
+    const int gsz = GM * tiles_n;
+    const int grp = o / gsz, within = o % gsz;
+    const int gm_here = (tiles_m - grp * GM) < GM ? (tiles_m - grp * GM) : GM;
+    const int tm = __builtin_amdgcn_readfirstlane(grp * GM + within % gm_here);
+    const int tn = __builtin_amdgcn_readfirstlane(within / gm_here);
+    const int64_t ch0 = (int64_t)tn * BN, tok0 = (int64_t)tm * BM;
+    const int64_t kb = a.m / 2;
+    const int nst = (int)(a.m / (2 * RB));
+
+    // DMA sources, as in dual_linear_pf (64-byte rows, 4-bit token rows)
+    const uint8_t *wbase = a.qw + ch0 * kb, *xbase = a.qx + tok0 * kb;
+    uint32_t off[DPT];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) {
+        const int q = j * NT + tid;
+        // odd 1 KB blocks (the second 16 rows of each 32-row block) have bit 0 of the
+        // chunk position flipped as well (see the reads below)
+        const int line = (q % (16 * CPR)) / 8, logical = (q % 8) ^ line ^ ((q / (16 * CPR)) & 1);
+        const int row = (q / (16 * CPR)) * 16 + 2 * line + logical / 4;
+        const int chunk = logical % 4;
+        int64_t rel;
+        if (row < BN) {
+            const int64_t ch = ch0 + row;
+            rel = (ch < a.n ? ch : a.n - 1) - ch0;
+        } else {
+            const int64_t tok = tok0 + (row - BN);
+            rel = (tok < a.b ? tok : a.b - 1) - tok0;
+        }
+        off[j] = (uint32_t)(row < BN ? qw_offset(rel, chunk * 16, a.m) : rel * kb + chunk * 16);
+    }
+    constexpr int SCL = STORE_ACC ? 0 : 4 * (BN + BM);
+    __shared__ __attribute__((aligned(16))) uint8_t ring[S * SLOT + SCL];
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wbase), 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(xbase), 0, 0x7fffffff, 0x00020000);
+    auto issue = [&](int st, auto slot) {
+        if constexpr (T16) {
+            if (st >= nst) {  // past the last stage: the first low-rank steps, into the slots it frees
+                pf_lr_issue<BN, BM, NT, SLOT, 0, true>(a, ch0, tok0, ring, decltype(slot)::value, st - nst, tid);
+                return;
+            }
+        }
+        uint8_t *dst = ring + decltype(slot)::value * SLOT;
+#pragma unroll
+        for (int j = 0; j < DPT; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((j * NT) / CPR < BN ? rw : rx,
+                                                     (__attribute__((address_space(3))) void *)(dst + (j * NT + wave_u * kWave) * 16),
+                                                     16, (int)off[j], st * RB * ((j * NT) / CPR < BN ? kPanelRows : 1), 0, 0);
+    };
+
+    v16i acc[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0;
+
+    // this lane's operand addresses for the stage halves h: row r32 of the wave's first
+    // 32-row block of weights (rda) and of tokens (rdb), chunk 2 h + kh; the second block
+    // is 2 KB further
+    const int r32 = lane & 31, kh = lane >> 5, li = r32 & 15;
+    uint32_t rda[2], rdb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t lane_off = (li / 2) * 128 + ((4 * (li % 2) + 2 * h + kh) ^ (li / 2) ^ (r32 / 16)) * 16 + (r32 / 16) * BLK;
+        rda[h] = lds_offset(ring) + lane_off + (wn * (BN / WN) / 16) * BLK;
+        rdb[h] = lds_offset(ring) + lane_off + ((BN + wm * (BM / WM)) / 16) * BLK;
+    }
+
+    if constexpr (SCL > 0) {
+        // s_W of the tile's channels and s_X of its tokens past the ring (one 4-byte load a
+        // thread; rows past n or b clamped), for the epilogue
+        const bool wv = wave_u < BN / kWave;
+        const int64_t idx = wv ? (ch0 + tid < a.n ? ch0 + tid : a.n - 1) : (tok0 + tid - BN < a.b ? tok0 + tid - BN : a.b - 1);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(wv ? a.sw : a.sx), 0,
+                                                                            (int)((wv ? a.n : a.b) * 4), 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)(ring + S * SLOT + wave_u * kWave * 4),
+                                                 4, (int)(idx * 4), 0, 0, 0);
+    }
+    // the main loop of dual_linear_pf: step st issues stage st into slot st % S and
+    // consumes stage st - (S - 1); every step issues, so each wait counts the same loads
+    for (int s0 = 0; s0 < nst + S - 1; s0 += S) {
+        static_for(std::make_integer_sequence<int, S>{}, [&](auto u) {
+            const int st = s0 + u, c = st - (S - 1);
+            if (c >= nst) return;
+            if (c >= 0) {
+                wait_vmcnt<(S - 2) * DPT>();
+                stage_barrier();  // stage c landed for every thread; stage c - 1 consumed by every wave
+            }
+            issue(T16 || st < nst ? st : nst - 1, u);
+            if (c < 0) return;
+            constexpr int OFF = ((u + 1) % S) * SLOT;  // slot of stage c
+            v4i raw[8];
+            lds_read_2x4<OFF, 2 * BLK>(rda[0], rda[1], rdb[0], rdb[1], raw);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                v4i alo[2], ahi[2], blo[2], bhi[2];
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    unpack16(raw[2 * h + f], alo[f], ahi[f]);
+                    unpack16(raw[4 + 2 * h + f], blo[f], bhi[f]);
+                }
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb) {
+                        acc[rb][cb] = mfma_i8_32(alo[rb], blo[cb], acc[rb][cb]);
+                        acc[rb][cb] = mfma_i8_32(ahi[rb], bhi[cb], acc[rb][cb]);
+                    }
+            }
+        });
+    }
+
+    // epilogue: lane coordinates recomputed from the thread index (see dual_linear_pf)
+    int te = tid;
+    asm volatile("" : "+v"(te));
+    const int r32e = te & 31, khe = (te >> 5) & 1;
+    const int64_t chw = ch0 + (wave_u % WN) * (BN / WN), tkw = tok0 + (wave_u / WN) * (BM / WM);
+    if constexpr (STORE_ACC) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t ch = chw + rb * 32 + 8 * q + 4 * khe;
+                    const int64_t tok = tkw + cb * 32 + r32e;
+                    if (ch < a.n && tok < a.b)
+                        *reinterpret_cast<v4i *>(a.acc + tok * a.n + ch) =
+                            v4i{acc[rb][cb][4 * q] >> 8, acc[rb][cb][4 * q + 1] >> 8, acc[rb][cb][4 * q + 2] >> 8,
+                                acc[rb][cb][4 * q + 3] >> 8};
+                }
+    } else {
+        // dequantize with the scales from LDS (the first wait of the main loop covered
+        // them), one 32-channel block at a time
+        const uint32_t sw_at = lds_offset(ring) + (uint32_t)((chw - ch0) + 4 * khe) * 4;
+        const uint32_t sx_at = lds_offset(ring) + (uint32_t)(BN + (tkw - tok0) + r32e) * 4;
+        v16f y[2][2];
+        static_for(std::make_integer_sequence<int, 2>{}, [&](auto rb) {
+            v4f swr[4];
+            float sxr[2];
+            lds_read_scales32<S * SLOT + 128 * decltype(rb)::value, S * SLOT>(sw_at, sx_at, swr, sxr);
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    y[rb][cb][v] = sxr[cb] * (swr[v / 4][v % 4] * (float)(acc[rb][cb][v] >> 8));
+                // one block at a time: the scheduler would otherwise start every block at
+                // once and run out of registers
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+        if constexpr (T16) {
+            // the ring's read addresses again, from the recomputed lane coordinates
+            const int lie = r32e & 15;
+            uint32_t ea[2], eb[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t lane_off =
+                    (lie / 2) * 128 + ((4 * (lie % 2) + 2 * h + khe) ^ (lie / 2) ^ (r32e / 16)) * 16 + (r32e / 16) * BLK;
+                ea[h] = lds_offset(ring) + lane_off + (uint32_t)((chw - ch0) / 16) * BLK;
+                eb[h] = lds_offset(ring) + lane_off + (uint32_t)((BN + (tkw - tok0)) / 16) * BLK;
+            }
+            pf32_lowrank_ring<S, SLOT, DPT>(a, y, ch0, tok0, ea, eb, khe, ring, te, nst);
+        } else {
+            pf32_lowrank_regs(a, y, chw, tkw, r32e, khe);
+        }
+        pf32_store(a, y, chw, tkw, r32e, khe);
+    }
+}
+
+template <int S, int GM, bool STORE_ACC, bool T16>
+static hipError_t launch_pf32_kernel(const DualArgs &a, hipStream_t stream) {
+    const int64_t tiles_n = (a.n + 127) / 128, tiles_m = (a.b + 127) / 128;
+    hipLaunchKernelGGL((dual_linear_pf32<S, GM, STORE_ACC, T16>), dim3((unsigned)(tiles_n * tiles_m)), dim3(256), 0, stream,
+                       a, (int)tiles_n, (int)tiles_m);
+    return hipGetLastError();
 }
 
 template <int BN, int BM, int WN, int WM, int S, int GM, int RB, bool STORE_ACC, bool LR4 = false, bool GRP = false,
@@ -1105,12 +1378,14 @@ static hipError_t launch_pf_kernel(const DualArgs &a, hipStream_t stream) {
 }
 
 // Many tokens: 128 x 128 tiles, XCD groups of 8 token tiles (the fastest exact variant
-// measured on MI355X for the gate/up and down shapes). The per-token W4A4 kernel runs a
-// two-stage ring at four CTAs per compute unit once the grid has at least 4 x 256 tiles,
-// and a three-stage ring at three CTAs below that, where the fourth slots would stay
-// partly empty and the deeper ring hides more latency (measured: 3-5% faster above, 1-5%
-// slower below, on 13 prefill shapes). The debug accumulator path follows the same rule,
-// so it checks the main loop that the same shape runs for Y.
+// measured on MI355X for the gate/up and down shapes; 4 and 16 were no faster on the 32 x 32
+// kernel). The per-token 4-bit layer runs dual_linear_pf32: a two-stage ring at four CTAs
+// per compute unit once the grid has at least 4 x 256 tiles, and a three-stage ring at
+// three CTAs below that, where the fourth slots would stay partly empty and the deeper ring
+// hides more latency (measured on the 16 x 16 kernel: 3-5% faster above, 1-5% slower below,
+// on 13 prefill shapes; three stages measured 2.6%, 5.6% and 5.9% slower on the 70B
+// gate/up, down and gate/up shapes with the 32 x 32 kernel). The exact accumulator export
+// follows the same rule, so it checks the main loop that the same shape runs for Y.
 static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
     constexpr int BN = 128, BM = 128, WN = 2, WM = 2, GM = 8, RB = 64;
     const int64_t tiles = ((a.n + BN - 1) / BN) * ((a.b + BM - 1) / BM);
@@ -1119,17 +1394,14 @@ static hipError_t launch_pf(const DualArgs &a, hipStream_t stream) {
         return a.acc ? launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, true, false, false, true>(a, stream)
                      : launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, false, false, false, true>(a, stream);
     if (a.acc)
-        return four ? launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, true>(a, stream)
-                    : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, true>(a, stream);
+        return four ? launch_pf32_kernel<2, GM, true, false>(a, stream) : launch_pf32_kernel<3, GM, true, false>(a, stream);
     if (a.group)
         return a.t16 ? launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, false, true, false, true>(a, stream)
                      : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, false, true>(a, stream);
     if (a.lr4) return launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, true>(a, stream);
-    if (a.t16)  // T as fp16: the low-rank operands go through the ring (pf_lowrank_ring)
-        return four ? launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, false, false, false, false, true>(a, stream)
-                    : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false, false, false, false, true>(a, stream);
-    return four ? launch_pf_kernel<BN, BM, WN, WM, 2, GM, RB, false>(a, stream)
-                : launch_pf_kernel<BN, BM, WN, WM, 3, GM, RB, false>(a, stream);
+    if (a.t16)  // T as fp16: the low-rank operands go through the ring (pf32_lowrank_ring)
+        return four ? launch_pf32_kernel<2, GM, false, true>(a, stream) : launch_pf32_kernel<3, GM, false, true>(a, stream);
+    return four ? launch_pf32_kernel<2, GM, false, false>(a, stream) : launch_pf32_kernel<3, GM, false, false>(a, stream);
 }
 
 hipError_t launch_dual_linear(const DualArgs &a, hipStream_t stream) {

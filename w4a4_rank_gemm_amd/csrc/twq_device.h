@@ -11,6 +11,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 constexpr float kQMax = 7.0f;  // 2^(k-1) - 1 for k = 4 (TwinQuant page 1, section 2, eq. (1))
@@ -144,6 +146,17 @@ __device__ __forceinline__ v4f mfma_f16(const v8h a, const v8h b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// 32 x 32 blocks: lane l supplies row l % 32 of each operand (16 int8 or 8 fp16 of one
+// K run); lane l holds column l % 32 of the result, and its register v the row
+// 8 (v / 4) + 4 (l / 32) + v % 4.
+__device__ __forceinline__ v16i mfma_i8_32(const v4i a, const v4i b, v16i c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16f mfma_f16_32(const v8h a, const v8h b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 // 16 bytes that one launch reads exactly once (the few-token weight stream): a
 // non-temporal load, so the stream does not displace from L2 the lines every CTA
 // re-reads (measured on MI355X: decode kernels 2.4-8.5% faster).
@@ -201,6 +214,45 @@ __device__ __forceinline__ void lds_read_4x4(uint32_t a, uint32_t b, v4i (&r)[8]
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
         : "v"(a), "v"(b), "n"(OFF), "n"(OFF + BLK), "n"(OFF + 2 * BLK), "n"(OFF + 3 * BLK)
+        : "memory");
+}
+
+// The eight operand reads of one stage of 32 x 32 blocks: from each of the addresses
+// a0, a1 (weight rows, the two halves of the stage) and b0, b1 (token rows), the blocks
+// at OFF and OFF + STR, completed before returning, for the same reason and in the same
+// way as lds_read_4x4. r = {a0, a0 + STR, a1, a1 + STR, b0, b0 + STR, b1, b1 + STR}.
+template <int OFF, int STR>
+__device__ __forceinline__ void lds_read_2x4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, v4i (&r)[8]) {
+    static_assert(OFF >= 0 && OFF + STR < 65536, "ds_read immediate offset");
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%12\n\t"
+        "ds_read_b128 %1, %8 offset:%13\n\t"
+        "ds_read_b128 %2, %9 offset:%12\n\t"
+        "ds_read_b128 %3, %9 offset:%13\n\t"
+        "ds_read_b128 %4, %10 offset:%12\n\t"
+        "ds_read_b128 %5, %10 offset:%13\n\t"
+        "ds_read_b128 %6, %11 offset:%12\n\t"
+        "ds_read_b128 %7, %11 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "n"(OFF), "n"(OFF + STR)
+        : "memory");
+}
+
+// Four operand reads: the blocks at OFF and OFF + STR from address a and from address b,
+// completed before returning, for the same reason and in the same way as lds_read_4x4.
+// r = {a, a + STR, b, b + STR}.
+template <int OFF, int STR>
+__device__ __forceinline__ void lds_read_2x2(uint32_t a, uint32_t b, v4i (&r)[4]) {
+    static_assert(OFF >= 0 && OFF + STR < 65536, "ds_read immediate offset");
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%6\n\t"
+        "ds_read_b128 %1, %4 offset:%7\n\t"
+        "ds_read_b128 %2, %5 offset:%6\n\t"
+        "ds_read_b128 %3, %5 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a), "v"(b), "n"(OFF), "n"(OFF + STR)
         : "memory");
 }
 
@@ -293,6 +345,27 @@ __device__ __forceinline__ void lds_read_scales(uint32_t w, uint32_t x, v4f (&sw
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(sw[0]), "=&v"(sw[1]), "=&v"(sw[2]), "=&v"(sw[3]), "=&v"(sx[0]), "=&v"(sx[1]), "=&v"(sx[2]), "=&v"(sx[3])
         : "v"(w), "v"(x), "n"(OFF), "n"(OFF + 64), "n"(OFF + 128), "n"(OFF + 192)
+        : "memory");
+}
+
+// Per-channel and per-token scales of one 32-channel block of a wave's 2 x 2 blocks of
+// 32 x 32: four 16-byte reads from address w plus OW (s_W of channels 8q + 4 (l / 32)
+// .. + 3, q = 0..3, 32 bytes apart) and two 4-byte reads from address x plus OX (s_X of
+// token l % 32 of each 32-token block, 128 bytes apart), completed before returning for
+// the same reason and in the same way as lds_read_4x4.
+template <int OW, int OX>
+__device__ __forceinline__ void lds_read_scales32(uint32_t w, uint32_t x, v4f (&sw)[4], float (&sx)[2]) {
+    static_assert(OW >= 0 && OW + 96 < 65536 && OX >= 0 && OX + 128 < 65536, "ds_read immediate offset");
+    asm volatile(
+        "ds_read_b128 %0, %6 offset:%8\n\t"
+        "ds_read_b128 %1, %6 offset:%9\n\t"
+        "ds_read_b128 %2, %6 offset:%10\n\t"
+        "ds_read_b128 %3, %6 offset:%11\n\t"
+        "ds_read_b32 %4, %7 offset:%12\n\t"
+        "ds_read_b32 %5, %7 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(sw[0]), "=&v"(sw[1]), "=&v"(sw[2]), "=&v"(sw[3]), "=&v"(sx[0]), "=&v"(sx[1])
+        : "v"(w), "v"(x), "n"(OW), "n"(OW + 32), "n"(OW + 64), "n"(OW + 96), "n"(OX), "n"(OX + 128)
         : "memory");
 }
 
