@@ -43,7 +43,10 @@ def _run(d):
 SHAPES = [(16, 4096, 4096, 32), (16, 512, 512, 16), (1, 4096, 272, 32), (5, 2048, 16384, 64),
           (16, 8192, 1024, 128), (24, 4096, 4096, 32), (32, 1024, 8192, 64), (48, 2048, 512, 16),
           (64, 4096, 2048, 32), (200, 1024, 528, 48), (16, 4096, 4096, 0), (3, 16384, 256, 256),
-          (29, 4096, 12304, 32)]  # 2x2 blocks reading Q_X from LDS with T's slices in the epilogue
+          (29, 4096, 12304, 32),  # 2x2 blocks reading Q_X from LDS with T's slices in the epilogue
+          # many tokens on grids of at least 4 x 256 tiles (the two-stage ring of the 32 x 32
+          # kernel): ragged tokens and channels, a single K stage, a half low-rank step (r = 48)
+          (1000, 128, 16400, 48), (1100, 384, 15008, 16)]
 
 
 @pytest.mark.parametrize("b,m,n,r", SHAPES)
