@@ -6,18 +6,19 @@
 // the residual partial sums and the low-rank product live only in registers and
 // are merged in one epilogue that stores fp16 once.
 //
-// Two main loops with the same epilogue arithmetic: dual_linear_decode for few tokens
-// (HBM-bound, operands straight from global memory) and dual_linear_pf for many tokens
-// (matrix-core-bound, operands staged through an LDS ring). Both expand packed int4
-// codes to int8 (x16, see unpack16) and issue v_mfma_i32_16x16x64_i8 -- gfx950 has no
-// int4 matrix instruction. The accumulator holds 256 * acc exactly (|acc| <= 49 m,
-// m <= 131072). Both also run the group-wise (GRP) and W4A8 (A8) variants described
-// at each kernel.
+// Main loops with the same epilogue arithmetic: dual_linear_decode for few tokens
+// (HBM-bound, operands straight from global memory) and, for many tokens
+// (matrix-core-bound, operands staged through an LDS ring), dual_linear_pf and its
+// 32 x 32-block form dual_linear_pf32, which the per-token 4-bit layer runs. All expand
+// packed int4 codes to int8 (x16, see unpack16) and issue v_mfma_i32_16x16x64_i8 (or
+// v_mfma_i32_32x32x32_i8) -- gfx950 has no int4 matrix instruction. The accumulator
+// holds 256 * acc exactly (|acc| <= 49 m, m <= 131072). The group-wise (GRP), W4A8
+// (A8) and int4 low-rank (LR4) variants are described at each kernel.
 //
 // Epilogue: acc is dequantized in place to fp32, then used as the C operand of
-// v_mfma_f32_16x16x32_f16 over the rank dimension with A = L2^T rows and
+// v_mfma_f32_16x16x32_f16 (v_mfma_f32_32x32x16_f16) over the rank dimension with A = L2^T rows and
 // B = T rows (rounded to fp16), so the two branches merge without a second
-// accumulator set. The i32 and f32 16x16 results share one register layout. In
+// accumulator set. The i32 and f32 results of one block shape share one register layout. In
 // the int4 low-rank variant the epilogue instead adds s_H (Q_H Q_L2^T), a second
 // int8 matrix product over the rank dimension.
 #include <utility>
