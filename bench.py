@@ -137,9 +137,13 @@ def host_env(torch):
     """Where the numbers were taken: GPU name, ROCm and HIP versions, torch, host CPU."""
     try:
         gpu = torch.cuda.get_device_name(0)
+        props = torch.cuda.get_device_properties(0)
+        arch = getattr(props, "gcnArchName", None)
+        units = props.multi_processor_count
     except Exception:  # noqa: BLE001 - informative only
-        gpu = None
-    return {"gpu": gpu, "rocm": rocm_version(), "hip": getattr(torch.version, "hip", None),
+        gpu, arch, units = None, None, None
+    return {"gpu": gpu, "gpu_arch": arch, "compute_units": units, "rocm": rocm_version(),
+            "hip": getattr(torch.version, "hip", None),
             "torch": torch.__version__, "host_cpu": cpu_model(), "host_threads": os.cpu_count()}
 
 
