@@ -46,7 +46,9 @@ SHAPES = [(16, 4096, 4096, 32), (16, 512, 512, 16), (1, 4096, 272, 32), (5, 2048
           (29, 4096, 12304, 32),  # 2x2 blocks reading Q_X from LDS with T's slices in the epilogue
           # many tokens on grids of at least 4 x 256 tiles (the two-stage ring of the 32 x 32
           # kernel): ragged tokens and channels, a single K stage, a half low-rank step (r = 48)
-          (1000, 128, 16400, 48), (1100, 384, 15008, 16)]
+          (1000, 128, 16400, 48), (1100, 384, 15008, 16),
+          # the three-stage ring with a single K stage
+          (300, 128, 272, 48)]
 
 
 @pytest.mark.parametrize("b,m,n,r", SHAPES)

@@ -149,7 +149,7 @@ RAGGED = [
     # few-token slices of 128 chunks staged through LDS
     (3, 32768, 48, 32), (16, 16512, 64, 16), (130, 20480, 80, 16), (16, 8192, 96, 32),
     # many tokens on grids of at least 4 x 256 tiles (two-stage ring), ragged edges
-    (1000, 128, 16400, 48),
+    (1000, 128, 16400, 48), (300, 128, 272, 48),
 ]
 
 
