@@ -302,12 +302,13 @@ twq_status twq_pack_lowrank_int4(const void *l1t, const void *l2t, int64_t r, in
                                  void *ql1, float *sl1, void *ql2, float *sl2, float *c, void *stream);
 
 /*
- * The activation side of the int4 low-rank branch: per-token quantization of X (as
- * twq_quantize_act, one launch), then H = Q_X Q_L1^T (exact, int32 on int8 matrix
- * cores) requantized on chip as described above, by CTAs that each hold every rank of
- * their tokens (TwinQuant page 1, section 4.3: the low-rank intermediate is
- * requantized on the fly and never written to global memory). Only Q_H and s_H are
- * stored.
+ * The activation side of the int4 low-rank branch: per-token quantization of X (the
+ * codes and scales of twq_quantize_act), then H = Q_X Q_L1^T (exact, int32 on int8
+ * matrix cores) requantized on chip as described above, by CTAs that each hold every
+ * rank of their tokens (TwinQuant page 1, section 4.3: the low-rank intermediate is
+ * requantized on the fly and never written to global memory). Only Q_X, s_X, Q_H and
+ * s_H are stored. Up to 256 tokens this is one launch (each CTA first quantizes its one
+ * token); above, the quantizer is a launch of its own.
  *   x     fp16 [b][m];  ql1, c  from twq_pack_lowrank_int4;  r a multiple of 32, 32..256
  *   qx    u8  [b][m/2]  (out)          packed Q_X
  *   sx    f32 [b]       (out)          s_X per token
@@ -337,7 +338,8 @@ twq_status twq_dual_linear_lr4(const void *qx, const float *sx, const void *qw, 
 
 /*
  * The whole layer with the int4 low-rank branch in one call: twq_quantize_act_lr4 then
- * twq_dual_linear_lr4 (three launches), with Q_X, s_X, Q_H and s_H kept in the workspace.
+ * twq_dual_linear_lr4 (two launches up to 256 tokens, three above), with Q_X, s_X, Q_H and
+ * s_H kept in the workspace.
  * Y is bitwise the result of those two calls.
  *   x fp16 [b][m]; qw, sw from twq_pack_weight; ql1, c, ql2 from twq_pack_lowrank_int4;
  *   r a multiple of 32, 32..256; y fp16 [b][n] (out)

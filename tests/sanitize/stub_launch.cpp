@@ -125,10 +125,18 @@ hipError_t launch_pack_lowrank(const uint16_t *l1t, const uint16_t *l2t, int r, 
     return hipSuccess;
 }
 
-hipError_t launch_lowrank_requant(const uint8_t *qx, const float *sx, const uint8_t *ql1, const float *c, int r,
+bool lowrank_requant_quantizes(int64_t b) { return b <= 256; }
+
+hipError_t launch_lowrank_requant(const uint16_t *x, uint8_t *qx, float *sx, const uint8_t *ql1, const float *c, int r,
                                   uint8_t *qh, float *sh, int32_t *h, int64_t b, int64_t m, hipStream_t) {
     if (b == 0) return hipSuccess;
     if (r < 32 || r > 256 || r % 32) return hipErrorInvalidValue;
+    if (x && b > 256) return hipErrorInvalidValue;
+    if (x) {
+        touch_read(x, (size_t)b * (size_t)m * 2);
+        touch_write(qx, (size_t)b * (size_t)m / 2);
+        touch_write(sx, (size_t)b * 4);
+    }
     touch_read(qx, (size_t)b * (size_t)m / 2);
     touch_read(sx, (size_t)b * 4);
     touch_read(ql1, (size_t)r * (size_t)m / 2);

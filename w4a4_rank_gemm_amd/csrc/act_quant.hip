@@ -27,30 +27,6 @@ struct ActDev {
     int jq;          // chunks of a row per thread (0: rows past 16384 elements)
 };
 
-__device__ __forceinline__ uint32_t absmax8_bits(const uint4 c, uint32_t mx) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        // |x| of an fp16 is its bit pattern without the sign; for finite values the
-        // integer order of these patterns is the order of the magnitudes
-        uint32_t lo = w[e] & 0x7FFFu, hi = (w[e] >> 16) & 0x7FFFu;
-        mx = mx > lo ? mx : lo;
-        mx = mx > hi ? mx : hi;
-    }
-    return mx;
-}
-
-__device__ __forceinline__ uint32_t quant8(const uint4 c, float s, float inv) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    int q[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        q[2 * e] = quant_code_fast(half_bits_to_float(w[e] & 0xFFFFu), s, inv);
-        q[2 * e + 1] = quant_code_fast(half_bits_to_float(w[e] >> 16), s, inv);
-    }
-    return pack8(q);
-}
-
 // Eight 8-bit codes (q_max = 127) of one 16-byte chunk of fp16, one byte each in order.
 __device__ __forceinline__ uint2 quant8_a8(const uint4 c, float s, float inv) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};

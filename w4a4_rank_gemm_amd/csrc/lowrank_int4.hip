@@ -7,8 +7,8 @@
 //    row t, by eq. (1) (page 1, section 2); c_t = s_L1[t] s_L2[t] is what the second
 //    GEMM cannot carry inside its integer sum over t;
 //  * H = Q_X Q_L1^T and its requantization, per token h_t = (s_X H_t) c_t in binary32,
-//    s_H = max_t |h_t| / 7, Q_H = round(h / s_H), happen on chip in the activation
-//    launch (act_rows in act_quant.hip), which stores only Q_H and s_H;
+//    s_H = max_t |h_t| / 7, Q_H = round(h / s_H), happen on chip in lr4_requant_kernel
+//    below, which stores only Q_H and s_H (and, with few tokens, quantizes X first);
 //  * the fused kernel's epilogue then adds s_H (Q_H Q_L2) (dual_linear.hip).
 #include "twq_device.h"
 #include "twq_kernels.h"
@@ -92,8 +92,9 @@ __global__ __launch_bounds__(kLrThreads) void lr_pack_l2_kernel(const uint16_t *
 // token's ranks. Only Q_H and s_H are written (and H itself for the test export): H
 // never reaches global memory (TwinQuant page 1, section 4.3).
 struct RequantArgs {
-    const uint8_t *qx;   // [b][m / 2] packed
-    const float *sx;     // [b]
+    const uint8_t *qx;   // [b][m / 2] packed (written first by the kernel when x is set)
+    const float *sx;     // [b] (likewise)
+    const uint16_t *x;   // fp16 [b][m], or NULL: one token a CTA quantizes its own row first
     const uint8_t *ql1;  // panel layout, r rows
     const float *c;      // [r]
     int r;
@@ -111,10 +112,15 @@ constexpr int req_batch(int nr, int tb) {  // steps per batch: two batches and t
                                                                 : (170 - 4 * nr * tb) / (8 * (nr + tb));
 }
 
-template <int TB, int NR, bool STORE_H>
+// QX (one token a CTA): the CTA first quantizes its token's row by eq. (1) exactly as the
+// activation quantizer does (amax over the fp16 bit patterns, s_X = amax / 7 correctly
+// rounded, quant_code_fast), writes Q_X and s_X, and meets before the H loop reads them
+// back; so the few-token call needs no separate quantizer launch.
+template <int TB, int NR, bool STORE_H, bool QX = false>
 __global__ __launch_bounds__(kReqWaves * 64) void lr4_requant_kernel(RequantArgs a) {
 #pragma clang fp contract(off)
     constexpr int NW = kReqWaves, NT = NW * 64, BM = 16 * TB, U = req_batch(NR, TB);
+    static_assert(!QX || TB == 1, "the row quantizer takes one token a CTA");
     constexpr int HP = NR * 16 + 1;        // LDS row pitch of H in words (odd: no bank conflicts)
     constexpr int TPT = NT / BM;           // threads per token in the requantization
     constexpr int RPT = NR * 16 / TPT >= 2 ? NR * 16 / TPT : 2;  // ranks per thread (an even count)
@@ -127,6 +133,27 @@ __global__ __launch_bounds__(kReqWaves * 64) void lr4_requant_kernel(RequantArgs
     const int64_t tok0 = (int64_t)blockIdx.x * tpc, b = a.b, m = a.m;
     const int nr = a.r / 16;
     for (int i = tid; i < BM * HP; i += NT) hs[i] = 0;
+    if constexpr (QX) {
+        // the CTA's one token (tpc = 1, blockIdx.x < b): its row's codes and scale
+        __shared__ uint32_t red[NW];
+        const uint4 *xr = reinterpret_cast<const uint4 *>(a.x + tok0 * m);
+        const int64_t nch = m / 8;
+        uint32_t mx = 0;
+        for (int64_t c = tid; c < nch; c += NT) mx = absmax8_bits(xr[c], mx);
+        mx = wave_max_u32(mx);
+        if (lane == 0) red[wave] = mx;
+        __syncthreads();
+        uint32_t m4 = red[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) m4 = m4 > red[w] ? m4 : red[w];
+        const float amax = half_bits_to_float(m4);
+        const float s = amax / kQMax;  // correctly rounded binary32 division
+        const float inv = 1.0f / s;    // only used when amax > 0
+        uint32_t *qrow = reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(a.qx) + tok0 * (m / 2));
+        for (int64_t c = tid; c < nch; c += NT) qrow[c] = amax == 0.0f ? 0u : quant8(xr[c], s, inv);
+        if (tid == 0) const_cast<float *>(a.sx)[tok0] = s;
+        __syncthreads();  // Q_X and s_X of the token written for every thread of the CTA
+    }
 
     // this lane's operand addresses: rank block rb (past the live ones: the last live one,
     // unused) and token block tb (rows past b: the last row, never stored)
@@ -258,34 +285,39 @@ __global__ __launch_bounds__(kReqWaves * 64) void lr4_requant_kernel(RequantArgs
     }
 }
 
-template <int TB, bool STORE_H>
+template <int TB, bool STORE_H, bool QX = false>
 static hipError_t launch_requant_tb(const RequantArgs &a, hipStream_t s) {
     const int nr = a.r / 16;  // the kernel's NR bounds the live rank blocks
     const dim3 grid((unsigned)((a.b + a.tpc - 1) / a.tpc)), block(kReqWaves * 64);
     if (nr <= 2)
-        hipLaunchKernelGGL((lr4_requant_kernel<TB, 2, STORE_H>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((lr4_requant_kernel<TB, 2, STORE_H, QX>), grid, block, 0, s, a);
     else if (nr <= 4)
-        hipLaunchKernelGGL((lr4_requant_kernel<TB, 4, STORE_H>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((lr4_requant_kernel<TB, 4, STORE_H, QX>), grid, block, 0, s, a);
     else if (nr <= 8)
-        hipLaunchKernelGGL((lr4_requant_kernel<TB, 8, STORE_H>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((lr4_requant_kernel<TB, 8, STORE_H, QX>), grid, block, 0, s, a);
     else if constexpr (TB == 1)
-        hipLaunchKernelGGL((lr4_requant_kernel<1, 16, STORE_H>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((lr4_requant_kernel<1, 16, STORE_H, QX>), grid, block, 0, s, a);
     else
         return hipErrorInvalidValue;  // the launcher takes 16-token tiles above 128 ranks
     return hipGetLastError();
 }
 
-hipError_t launch_lowrank_requant(const uint8_t *qx, const float *sx, const uint8_t *ql1, const float *c, int r,
+bool lowrank_requant_quantizes(int64_t b) { return b <= 256; }
+
+hipError_t launch_lowrank_requant(const uint16_t *x, uint8_t *qx, float *sx, const uint8_t *ql1, const float *c, int r,
                                   uint8_t *qh, float *sh, int32_t *h, int64_t b, int64_t m, hipStream_t stream) {
     if (b == 0) return hipSuccess;
     if (r < 32 || r > 256 || r % 32) return hipErrorInvalidValue;
     // 32-token tiles where that still gives every compute unit a tile (up to 128 ranks;
     // above, the sums of two token blocks would not fit the registers), else up to 16
-    // tokens a CTA, as few as gives 256 CTAs (one token a CTA at most 256 tokens)
+    // tokens a CTA, as few as gives 256 CTAs (one token a CTA at most 256 tokens, where
+    // the CTA also quantizes that token when x is given)
     const bool two = (b + 31) / 32 >= 256 && r <= 128;
     int64_t tpc = two ? 32 : (b + 255) / 256;
     if (tpc > 16 && !two) tpc = 16;
-    RequantArgs a{qx, sx, ql1, c, r, qh, sh, h, b, m, (int)tpc};
+    if (x && tpc != 1) return hipErrorInvalidValue;  // callers quantize first above 256 tokens
+    RequantArgs a{qx, sx, x, ql1, c, r, qh, sh, h, b, m, (int)tpc};
+    if (x) return h ? launch_requant_tb<1, true, true>(a, stream) : launch_requant_tb<1, false, true>(a, stream);
     if (h) return two ? launch_requant_tb<2, true>(a, stream) : launch_requant_tb<1, true>(a, stream);
     return two ? launch_requant_tb<2, false>(a, stream) : launch_requant_tb<1, false>(a, stream);
 }

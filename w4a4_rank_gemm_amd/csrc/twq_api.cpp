@@ -372,18 +372,24 @@ twq_status quantize_act_lr4_impl(const void *x, int64_t b, int64_t m, const void
     if (!aligned16(x) || !aligned16(ql1) || !aligned16(c) || !aligned16(qx) || !aligned16(sx) || !aligned16(qh) ||
         !aligned16(sh) || (h && !aligned16(h)))
         return TWQ_ERR_ALIGN;
-    // the per-token quantizer (no first low-rank product: r = 0), then H and Q_H on chip
-    twq::ActArgs a{};
-    a.x = static_cast<const uint16_t *>(x);
-    a.b = b;
-    a.m = m;
-    a.qx = static_cast<uint8_t *>(qx);
-    a.sx = sx;
+    // the per-token quantizer (no first low-rank product: r = 0), then H and Q_H on chip;
+    // with few tokens (one a CTA) the requantization kernel quantizes its token itself
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = twq::launch_act(a, twq::plan_act(b, m, 0), st);
+    hipError_t e = hipSuccess;
+    const bool fused = twq::lowrank_requant_quantizes(b);
+    if (!fused) {
+        twq::ActArgs a{};
+        a.x = static_cast<const uint16_t *>(x);
+        a.b = b;
+        a.m = m;
+        a.qx = static_cast<uint8_t *>(qx);
+        a.sx = sx;
+        e = twq::launch_act(a, twq::plan_act(b, m, 0), st);
+    }
     if (e == hipSuccess)
-        e = twq::launch_lowrank_requant(static_cast<const uint8_t *>(qx), sx, static_cast<const uint8_t *>(ql1), c,
-                                        (int)r, static_cast<uint8_t *>(qh), sh, h, b, m, st);
+        e = twq::launch_lowrank_requant(fused ? static_cast<const uint16_t *>(x) : nullptr, static_cast<uint8_t *>(qx), sx,
+                                        static_cast<const uint8_t *>(ql1), c, (int)r, static_cast<uint8_t *>(qh), sh, h,
+                                        b, m, st);
     return e == hipSuccess ? TWQ_OK : hip_fail(e, name);
 }
 

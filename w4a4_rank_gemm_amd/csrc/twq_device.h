@@ -70,6 +70,32 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
+// The running maximum mx of |x| over the eight fp16 values of a 16-byte chunk, as bit
+// patterns: |x| of an fp16 is its pattern without the sign, and for finite values the
+// integer order of these patterns is the order of the magnitudes.
+__device__ __forceinline__ uint32_t absmax8_bits(const uint4 c, uint32_t mx) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint32_t lo = w[e] & 0x7FFFu, hi = (w[e] >> 16) & 0x7FFFu;
+        mx = mx > lo ? mx : lo;
+        mx = mx > hi ? mx : hi;
+    }
+    return mx;
+}
+
+// The eight 4-bit codes of eq. (1) of a 16-byte chunk of fp16 (quant_code_fast), packed.
+__device__ __forceinline__ uint32_t quant8(const uint4 c, float s, float inv) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    int q[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        q[2 * e] = quant_code_fast(half_bits_to_float(w[e] & 0xFFFFu), s, inv);
+        q[2 * e + 1] = quant_code_fast(half_bits_to_float(w[e] >> 16), s, inv);
+    }
+    return pack8(q);
+}
+
 // max over the 64 lanes of a wave (every lane active), returned uniform: butterflies
 // within each row of 16 lanes by DPP moves (the two quad permutations, then the
 // half-row and the row mirror), then the four row maxima read from lanes 0, 16, 32

@@ -126,8 +126,10 @@ int hip_error(hipError_t e, const char *where);
 
 // H = Q_X Q_L1^T and its requantization on chip (lowrank_int4.hip): qx packed [b][m/2],
 // sx [b], ql1 in the panel layout (r rows), c [r]; writes qh [b][r/2], sh [b] and, if h
-// is not NULL, the exact H [b][r] (int32) as well.
-hipError_t launch_lowrank_requant(const uint8_t *qx, const float *sx, const uint8_t *ql1, const float *c, int r,
+// is not NULL, the exact H [b][r] (int32) as well. x (fp16 [b][m]) not NULL: the kernel
+// first writes qx and sx itself from x (only where lowrank_requant_quantizes(b)).
+bool lowrank_requant_quantizes(int64_t b);
+hipError_t launch_lowrank_requant(const uint16_t *x, uint8_t *qx, float *sx, const uint8_t *ql1, const float *c, int r,
                                   uint8_t *qh, float *sh, int32_t *h, int64_t b, int64_t m, hipStream_t stream);
 
 // ---- offline fold of given transforms into the split (fold.hip) ------------------------
