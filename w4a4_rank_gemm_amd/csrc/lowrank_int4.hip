@@ -92,8 +92,8 @@ __global__ __launch_bounds__(kLrThreads) void lr_pack_l2_kernel(const uint16_t *
 // token's ranks. Only Q_H and s_H are written (and H itself for the test export): H
 // never reaches global memory (TwinQuant page 1, section 4.3).
 struct RequantArgs {
-    const uint8_t *qx;   // [b][m / 2] packed (written first by the kernel when x is set)
-    const float *sx;     // [b] (likewise)
+    uint8_t *qx;         // [b][m / 2] packed (written first by the kernel when x is set)
+    float *sx;           // [b] (likewise)
     const uint16_t *x;   // fp16 [b][m], or NULL: one token a CTA quantizes its own row first
     const uint8_t *ql1;  // panel layout, r rows
     const float *c;      // [r]
@@ -149,9 +149,9 @@ __global__ __launch_bounds__(kReqWaves * 64) void lr4_requant_kernel(RequantArgs
         const float amax = half_bits_to_float(m4);
         const float s = amax / kQMax;  // correctly rounded binary32 division
         const float inv = 1.0f / s;    // only used when amax > 0
-        uint32_t *qrow = reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(a.qx) + tok0 * (m / 2));
+        uint32_t *qrow = reinterpret_cast<uint32_t *>(a.qx + tok0 * (m / 2));
         for (int64_t c = tid; c < nch; c += NT) qrow[c] = amax == 0.0f ? 0u : quant8(xr[c], s, inv);
-        if (tid == 0) const_cast<float *>(a.sx)[tok0] = s;
+        if (tid == 0) a.sx[tok0] = s;
         __syncthreads();  // Q_X and s_X of the token written for every thread of the CTA
     }
 
